@@ -1,0 +1,211 @@
+"""Benchmark: SDPA forward throughput of attn_flash on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one attention forward pass (kb_attention, variant flash) over the
+workload B=2, H=32, S=8192, d=128, bf16 inputs, causal mask, fp32 output,
+with Q, K, V already resident in HBM.  The K timed steps are bracketed by
+torch.cuda.synchronize() on both sides; inside, kb_bench_attention records a
+hipEvent between consecutive launches on the launch stream, which gives the
+per-launch kernel time used for the roofline fraction.
+
+The JSON line also carries:
+  roofline      achieved TFLOP/s per launch vs the MI355X dense bf16 MFMA
+                peak (2516.6 TFLOP/s), and HBM traffic per launch when the
+                --traffic-kib option gives the rocprofv3 counter reading;
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded,
+                seeded sample of the same workload's query rows (also used
+                to check the GPU output on those rows);
+  triad         the HBM triad calibration (best of a block-size sweep);
+  variants      naive and fused on the same workload (a few timed calls).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SDPA forward TFLOP/s + % of MFMA peak per (B,H,S,d), causal/non-causal"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="b2h32s8192d128_bf16_causal")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-extras", action="store_true", help="skip triad and the naive/fused variants")
+    ap.add_argument("--traffic-kib", type=float, nargs=2, metavar=("FETCH", "WRITE"), default=None,
+                    help="rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the flash kernel, "
+                         "already scaled by the copy-kernel calibration")
+    return ap.parse_args()
+
+
+def device_tensors(p, torch):
+    out = []
+    for a in p.device_arrays():
+        if a.dtype == np.uint16:
+            out.append(torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda())
+        else:
+            out.append(torch.from_numpy(a).cuda())
+    return out
+
+
+def cpu_baseline(p, o_gpu, budget_s, seed=1234):
+    """Time the fp64 oracle on seeded query rows until ~budget_s seconds."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    nthreads = oracle.default_threads()
+    flops = 0
+    rows_done = []
+    errs = []
+    t_used = 0.0
+    chunk = 256
+    while t_used < budget_s:
+        rows = rng.integers(0, p.BH * p.S, size=chunk).astype(np.int64)
+        t0 = time.perf_counter()
+        ref = oracle.sdpa(p.q, p.k, p.v, causal=p.causal, rows=rows, nthreads=nthreads)
+        t_used += time.perf_counter() - t0
+        i = rows % p.S
+        vis = (i + 1) if p.causal else np.full_like(i, p.S)
+        flops += int(4 * p.d * vis.sum())
+        rows_done.append(rows)
+        errs.append(float(np.max(np.abs(o_gpu[rows] - ref))))
+        if t_used > 0.5 * budget_s and chunk < 4096:
+            chunk *= 2
+    n = int(sum(len(r) for r in rows_done))
+    return {
+        "value": flops / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": f"{n} seeded query rows (of {p.BH * p.S}) of the same workload, fp64, "
+                  f"{t_used:.1f} s; throughput scaled by the rows' algorithmic FLOPs",
+        "max_abs_err_vs_gpu_on_sample": max(errs),
+    }
+
+
+def triad_calibration(kb, torch, stream):
+    n = 2048 * 1024 * 1024 // 12  # 2048 MiB working set over a, b, c
+    n -= n % 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda")
+    b = torch.rand(n, dtype=torch.float32, device="cuda")
+    c = torch.rand(n, dtype=torch.float32, device="cuda")
+    best = None
+    for block in (64, 128, 256, 512, 1024):
+        per, _ = kb.kb_bench_triad(a.data_ptr(), b.data_ptr(), c.data_ptr(), 1.5, n, block, stream, 20, 50)
+        ms = float(np.median(per))
+        gbs = 12.0 * n / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": gbs, "block": block, "median_ms": ms}
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"best_gbs": round(best["gbs"], 1), "block": best["block"], "bytes": 12 * n,
+            "calibration_vs_8000": round(best["gbs"] / HBM_PEAK_GBS, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no "
+              f"multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        return 2
+    import torch
+
+    import transformer_attention_micro_amd as kb
+    from transformer_attention_micro_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    kb.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    p = inputs.workload(args.workload)
+    q, k, v = device_tensors(p, torch)
+    o = torch.empty((p.BH, p.S, p.d), dtype=torch.float32, device="cuda")
+    dt = kb.KB_BF16 if p.dtype == inputs.BF16 else kb.KB_F32
+    cfg = kb.make_cfg(p.B, p.H, p.S, p.d, p.causal, dt)
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    flops = kb.attention_flops(p.B, p.H, p.S, p.d, p.causal)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
+
+    for _ in range(args.warmup):
+        kb.kb_attention(cfg, *ptrs, "flash", stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    per, total_ms = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, 0, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    kern_ms = float(np.mean(per))
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[p.dtype]
+    traffic = None
+    if args.traffic_kib:
+        traffic = int((args.traffic_kib[0] + args.traffic_kib[1]) * 1024)
+
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": p.B, "H": p.H, "S": p.S, "d": p.d,
+                   "causal": p.causal, "variant": "flash", "out": "f32", "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_min": round(float(np.min(per)), 4),
+                     "kernel_ms_p50": round(float(np.median(per)), 4),
+                     "kernel_ms_p99": round(float(np.percentile(per, 99)), 4)},
+    }
+
+    if not args.no_extras:
+        extras = {}
+        ws = torch.empty(kb.kb_attention_workspace_size(cfg, "naive"), dtype=torch.uint8, device="cuda")
+        ncfg = kb.make_cfg(p.B, p.H, p.S, p.d, p.causal, dt, 0.0, ws.data_ptr(), ws.numel())
+        for name, c in (("naive", ncfg), ("fused", cfg)):
+            try:
+                pv, _ = kb.kb_bench_attention(c, *ptrs, name, stream, 1, 3)
+                ms = float(np.median(pv))
+                extras[name] = {"ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+                if name == "naive":
+                    nbytes = 16 * p.BH * p.S * p.S + kb.attention_bytes(p.B, p.H, p.S, p.d, 2 if dt else 4)
+                    extras[name]["hbm_gbs_algorithmic"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            except kb.KbError as e:
+                extras[name] = {"error": str(e)}
+        del ws
+        torch.cuda.empty_cache()
+        result["variants"] = extras
+        result["triad"] = triad_calibration(kb, torch, stream)
+
+    if not args.no_cpu:
+        kb.kb_attention(cfg, *ptrs, "flash", stream)
+        torch.cuda.synchronize()
+        o_host = o.cpu().numpy().reshape(p.BH * p.S, p.d).astype(np.float64)
+        result["cpu_baseline"] = cpu_baseline(p, o_host, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

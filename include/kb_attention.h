@@ -1,0 +1,153 @@
+/*
+ * kb_attention.h: C ABI of the MI355X (gfx950) scaled dot-product attention
+ * forward library (libkb.so).
+ *
+ * What the library computes is defined on the page "kbench — Transformer
+ * Attention Micro-benchmark Harness", section "The three GPU kernels":
+ *
+ *     O = softmax(Q K^T / sqrt(d)) V
+ *
+ * over a flattened (batch * heads) axis, every tensor laid out
+ * [head, seq, dim] row-major.  The problem parameters (seq, dim, heads and
+ * the causal flag) are the fields the same page's harness sweeps (section
+ * "Running") and sends in its RUN_ATTN request (section "Architecture",
+ * sequence diagram).  "causal" is read as: key j is visible to query i iff
+ * j <= i (0-based), masked keys get weight exactly 0.
+ *
+ * The three variants are the page's three kernels (same section):
+ *   KB_NAIVE  three passes, the full S x S fp32 score matrix in HBM
+ *             (caller-provided workspace), row softmax in place, then P V;
+ *   KB_FUSED  one workgroup per query row, the row's scores held in LDS;
+ *   KB_FLASH  key/value tiles streamed through LDS with an online softmax
+ *             (running max m and denominator l), MFMA tiles for both
+ *             contractions, the score matrix never materialised.
+ * The HBM triad a[i] = b[i] + s * c[i] is the bandwidth calibration of the
+ * page "TileOPs-Metax benchmarks/hardware", section "HBM Bandwidth".
+ *
+ * Conventions for every entry point:
+ *   - Pointers named Q, K, V, O, a, b, c, workspace are DEVICE pointers
+ *     (hipMalloc / torch CUDA tensors); everything else is host memory.
+ *   - The caller owns every buffer.  The library allocates nothing that
+ *     outlives a call (the benchmark helpers create and destroy their own
+ *     hipEvents).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the default stream).  kb_attention and kb_triad do not synchronise.
+ *   - Arguments are validated before anything is launched.  Errors are
+ *     returned as a kb_status; nothing aborts or exits.  After a non-KB_OK
+ *     return, kb_last_error() gives a message for the calling thread.
+ *   - The library is stateless and may be called from several host threads.
+ */
+#ifndef KB_ATTENTION_H
+#define KB_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  KB_BF16 data is passed as raw 16-bit bfloat16 patterns. */
+typedef enum { KB_F32 = 0, KB_BF16 = 1 } kb_dtype;
+
+/* Kernel selector (kbench page, "The three GPU kernels"). */
+typedef enum { KB_NAIVE = 0, KB_FUSED = 1, KB_FLASH = 2 } kb_variant;
+
+typedef enum {
+  KB_OK = 0,
+  KB_ERR_INVALID = 1,     /* null pointer, non-positive size, bad enum value */
+  KB_ERR_UNSUPPORTED = 2, /* valid but not implemented (dim, dtype, LDS size) */
+  KB_ERR_WORKSPACE = 3,   /* naive: workspace missing or too small */
+  KB_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  KB_ERR_NO_DEVICE = 5    /* no usable gfx950 device */
+} kb_status;
+
+/*
+ * One attention problem.  Q, K, V are [batch*heads, seq, dim] row-major of
+ * type in_dtype; O is [batch*heads, seq, dim] row-major fp32.
+ *   batch, heads >= 1, seq >= 1 (any length: tails are masked),
+ *   dim in {32, 64, 128},
+ *   causal 0 or 1,
+ *   in_dtype KB_F32 or KB_BF16, out_dtype KB_F32 (the only output type),
+ *   scale: the logit scale; 0.0f means 1/sqrt(dim).  It is applied in fp32
+ *          to the fp32 dot products, never folded into the inputs.
+ *   workspace / workspace_bytes: device scratch, used by KB_NAIVE only
+ *          (>= kb_attention_workspace_size bytes, 256-byte aligned);
+ *          ignored by the other variants.
+ * batch * heads * seq * dim must stay below 2^31 elements per tensor, and
+ * batch * heads * seq * seq below 2^40 (naive workspace).
+ */
+typedef struct {
+  int32_t batch, heads, seq, dim;
+  int32_t causal;
+  int32_t in_dtype;  /* kb_dtype */
+  int32_t out_dtype; /* kb_dtype, KB_F32 */
+  float scale;
+  void *workspace;
+  size_t workspace_bytes;
+} kb_attn_cfg;
+
+/*
+ * Enqueue one attention forward pass of `variant` on `stream`.
+ * Returns KB_OK once the kernels are enqueued (not finished).
+ * KB_ERR_INVALID / KB_ERR_UNSUPPORTED / KB_ERR_WORKSPACE are returned before
+ * any launch; KB_ERR_HIP if a launch fails.  O may not alias Q, K or V.
+ */
+kb_status kb_attention(const kb_attn_cfg *cfg, const void *Q, const void *K, const void *V,
+                       void *O, int32_t variant, void *stream);
+
+/*
+ * Bytes of device workspace `variant` needs for `cfg`: 4 * B*H*S*S for
+ * KB_NAIVE (the fp32 score / probability matrix), 0 for the others, and
+ * (size_t)-1 if cfg is invalid.
+ */
+size_t kb_attention_workspace_size(const kb_attn_cfg *cfg, int32_t variant);
+
+/*
+ * HBM triad, a[i] = b[i] + s * c[i] for i < n (fp32, 128-bit accesses where
+ * alignment allows).  block: threads per workgroup, a multiple of 64 in
+ * [64, 1024].  a, b, c must not overlap.  Enqueued on `stream`.
+ */
+kb_status kb_triad(float *a, const float *b, const float *c, float s, size_t n, int32_t block,
+                   void *stream);
+
+/*
+ * Timing helper: `warmup` untimed launches of kb_attention, then `iters`
+ * timed ones, each bracketed by hipEvents recorded on `stream` (so the times
+ * cover exactly the kernels of one call, nothing else).  ms_per_iter (host,
+ * length iters) receives each call's GPU time; *ms_total the time from the
+ * first to the last event.  Synchronises `stream` before returning.
+ */
+kb_status kb_bench_attention(const kb_attn_cfg *cfg, const void *Q, const void *K, const void *V,
+                             void *O, int32_t variant, void *stream, int32_t warmup,
+                             int32_t iters, float *ms_per_iter, float *ms_total);
+
+/* The same protocol for kb_triad. */
+kb_status kb_bench_triad(float *a, const float *b, const float *c, float s, size_t n,
+                         int32_t block, void *stream, int32_t warmup, int32_t iters,
+                         float *ms_per_iter, float *ms_total);
+
+/* Properties of the current device, filled by kb_device_info. */
+typedef struct {
+  char arch[64];              /* e.g. "gfx950:sramecc+:xnack-" */
+  int32_t compute_units;
+  int32_t max_lds_per_block;  /* bytes of LDS one workgroup may use */
+  int32_t clock_mhz;          /* peak engine clock the runtime reports */
+  int32_t memory_clock_mhz;
+  int64_t global_mem_bytes;
+} kb_device_props;
+
+/* Query the current HIP device.  KB_ERR_NO_DEVICE without a device. */
+kb_status kb_device_info(kb_device_props *out);
+
+/* Static text for a status code (never NULL). */
+const char *kb_status_string(int32_t status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char *kb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KB_ATTENTION_H */

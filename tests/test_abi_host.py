@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (CPU only; nothing is launched).
+
+libkb.so must load here (no GPU), export every function include/kb_attention.h
+declares, and reject bad arguments before touching the device.  With valid
+arguments and no device the library must say so (KB_ERR_NO_DEVICE) instead of
+launching anything.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import transformer_attention_micro_amd as kb
+from transformer_attention_micro_amd import _lib
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "kb_attention.h"
+FAKE = 1 << 28  # aligned, non-NULL stand-in pointer; never dereferenced on these paths
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(kb_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTS)
+    lib = kb.lib()
+    for n in names:
+        assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n
+
+
+def test_status_strings():
+    for code in range(6):
+        assert kb.kb_status_string(code) and kb.kb_status_string(code) != "unknown status"
+    assert kb.kb_status_string(99) == "unknown status"
+
+
+def cfg(**kw):
+    base = dict(batch=2, heads=3, seq=100, dim=64, causal=False, dtype=kb.KB_BF16)
+    base.update(kw)
+    return kb.make_cfg(base["batch"], base["heads"], base["seq"], base["dim"], base["causal"], base["dtype"],
+                       base.get("scale", 0.0), base.get("workspace", 0), base.get("workspace_bytes", 0))
+
+
+def test_workspace_size():
+    assert kb.kb_attention_workspace_size(cfg(), "naive") == 4 * 2 * 3 * 100 * 100
+    assert kb.kb_attention_workspace_size(cfg(), "flash") == 0
+    assert kb.kb_attention_workspace_size(cfg(), "fused") == 0
+    with pytest.raises(kb.KbError):
+        kb.kb_attention_workspace_size(cfg(seq=0), "naive")
+
+
+def status_of(c, variant="flash", ptrs=(FAKE, FAKE * 2, FAKE * 3, FAKE * 4)):
+    try:
+        kb.kb_attention(c, *ptrs, variant)
+    except kb.KbError as e:
+        return e.status
+    return 0
+
+
+@pytest.mark.parametrize("bad", [dict(batch=0), dict(heads=-1), dict(seq=0), dict(dim=0),
+                                 dict(causal=2), dict(dtype=7), dict(scale=-1.0),
+                                 dict(scale=float("inf"))])
+def test_invalid_arguments(bad):
+    c = cfg(**{k: v for k, v in bad.items() if k != "causal"})
+    if "causal" in bad:
+        c.causal = bad["causal"]
+    assert status_of(c) == 1
+
+
+def test_null_pointers_and_bad_variant():
+    assert kb.lib().kb_attention(None, FAKE, FAKE, FAKE, FAKE, 2, None) == 1
+    assert status_of(cfg(), ptrs=(0, FAKE, FAKE, FAKE * 4)) == 1
+    assert status_of(cfg(), ptrs=(FAKE, FAKE * 2, FAKE * 3, 0)) == 1
+    assert status_of(cfg(), variant=3) == 1
+
+
+def test_unsupported_dims_and_sizes():
+    assert status_of(cfg(dim=48)) == 2
+    assert status_of(cfg(dim=256)) == 2
+    assert status_of(cfg(batch=1, heads=1, seq=1 << 24, dim=128)) == 2
+    c = cfg()
+    c.out_dtype = kb.KB_BF16
+    assert status_of(c) == 2
+
+
+def test_misaligned_or_overlapping_buffers():
+    assert status_of(cfg(), ptrs=(FAKE + 2, FAKE * 2, FAKE * 3, FAKE * 4)) == 1
+    # O overlapping Q
+    assert status_of(cfg(), ptrs=(FAKE, FAKE * 2, FAKE * 3, FAKE + 64)) == 1
+
+
+def test_naive_needs_workspace():
+    assert status_of(cfg(), variant="naive") == 3
+    c = cfg(workspace=FAKE * 8, workspace_bytes=4 * 2 * 3 * 100 * 100 - 1)
+    assert status_of(c, variant="naive") == 3
+    c = cfg(workspace=FAKE * 8 + 16, workspace_bytes=4 * 2 * 3 * 100 * 100)
+    assert status_of(c, variant="naive") == 3
+
+
+def test_valid_call_without_device_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert status_of(cfg()) == 5
+    assert "device" in kb.lib().kb_last_error().decode().lower() or kb.lib().kb_last_error()
+
+
+def test_triad_argument_checks():
+    lib = kb.lib()
+    assert lib.kb_triad(None, FAKE, FAKE, 1.0, 16, 256, None) == 1
+    assert lib.kb_triad(FAKE, FAKE * 2, FAKE * 3, 1.0, 0, 256, None) == 1
+    assert lib.kb_triad(FAKE, FAKE * 2, FAKE * 3, 1.0, 16, 100, None) == 1
+    assert lib.kb_triad(FAKE, FAKE * 2, FAKE * 3, 1.0, 16, 2048, None) == 1
+    assert lib.kb_triad(FAKE, FAKE + 8, FAKE * 3, 1.0, 16, 256, None) == 1
+
+
+def test_flop_and_byte_counts():
+    assert kb.attention_flops(1, 1, 64, 32, False) == 524288
+    assert kb.attention_flops(2, 32, 8192, 128, True) == 1099645845504
+    assert kb.attention_flops(1, 16, 32768, 128, False) == 8796093022208
+    assert kb.attention_bytes(1, 1, 64, 32, 4) == 32 * 1024

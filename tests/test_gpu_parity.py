@@ -1,0 +1,213 @@
+"""GPU parity: every variant of kb_attention against the fp64 oracle.
+
+Inputs are the seeded N(0, 1) problems of transformer_attention_micro_amd.inputs
+(bf16 problems rounded once on the host, so both sides see the same values).
+Outputs are pre-filled with NaN so an element the kernels never write fails.
+Small and medium problems are compared on every element; the large ones on
+the tile-edge rows of every head plus 64 seeded rows per head, computed by the
+oracle one row at a time.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import transformer_attention_micro_amd as kb
+from transformer_attention_micro_amd import inputs
+from tests.gpu_util import (compare, nan_output, oracle_full, oracle_rows, sample_rows, to_device,
+                            torch_cuda)
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = ("naive", "fused", "flash")
+_oracle_cache = {}
+_problems = {}
+
+
+def workload(name, seed=0):
+    """Named workloads are drawn once per session (the large ones take seconds)."""
+    if (name, seed) not in _problems:
+        _problems[(name, seed)] = inputs.workload(name, seed=seed)
+    return _problems[(name, seed)]
+
+
+def run(p, variant, **kw):
+    torch = torch_cuda()
+    q, k, v = to_device(p)
+    o = nan_output(p)
+    kb.attention(q, k, v, o, causal=p.causal, variant=variant, heads=p.H, **kw)
+    torch.cuda.synchronize()
+    return o
+
+
+def full_check(p, variant, label):
+    key = (p.B, p.H, p.S, p.d, p.dtype, p.causal, p.seed, p.q_scale)
+    if key not in _oracle_cache:
+        _oracle_cache[key] = oracle_full(p)
+    o = run(p, variant).cpu().numpy()
+    return compare(o, _oracle_cache[key], p.dtype, label)
+
+
+def sampled_check(p, variant, label, seed=0):
+    rows = sample_rows(p.S, p.BH, seed)
+    key = (p.B, p.H, p.S, p.d, p.dtype, p.causal, p.seed, p.q_scale, "rows", seed)
+    if key not in _oracle_cache:
+        _oracle_cache[key] = oracle_rows(p, rows)
+    o = run(p, variant).cpu().numpy().reshape(p.BH * p.S, p.d)
+    assert np.all(np.isfinite(o)), f"{label}: non-finite output somewhere"
+    return compare(o[rows], _oracle_cache[key], p.dtype, label)
+
+
+# ---------------------------------------------------------------- the workloads
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_b1h1s64d32_f32(variant):
+    p = workload("b1h1s64d32_f32")
+    full_check(p, variant, f"b1h1s64d32_f32/{variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_b1h8s512d64_f32(variant, causal):
+    name = "b1h8s512d64_f32" + ("_causal" if causal else "")
+    for seed in (0, 1, 2):
+        p = workload(name, seed=seed)
+        full_check(p, variant, f"{name}/seed{seed}/{variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_b4h16s2048d64_bf16_causal(variant):
+    p = workload("b4h16s2048d64_bf16_causal")
+    full_check(p, variant, f"b4h16s2048d64_bf16_causal/{variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("name", ["b2h32s8192d128_bf16_causal", "b2h32s8192d128_bf16_causal_q8"])
+def test_b2h32s8192d128(variant, name):
+    p = workload(name)
+    sampled_check(p, variant, f"{name}/{variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_b1h16s32768d128_bf16(variant):
+    p = workload("b1h16s32768d128_bf16")
+    try:
+        sampled_check(p, variant, f"b1h16s32768d128_bf16/{variant}")
+    except kb.KbError as e:
+        # fused needs 4*S bytes of LDS per row; the library reports when the
+        # device cannot hold it (never silently).
+        if variant == "fused" and e.status == 2:
+            pytest.skip(str(e))
+        raise
+
+
+# ---------------------------------------------------------------- ragged and tiny shapes
+
+TINY_S = (1, 2, 3, 17, 31, 33, 64, 65, 127, 129, 200)
+
+
+@pytest.mark.parametrize("dtype", [inputs.F32, inputs.BF16])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_ragged_shapes(dtype, d, causal, variant):
+    for S in TINY_S:
+        p = inputs.make_problem(1, 3, S, d, dtype, causal=causal, seed=S)
+        full_check(p, variant, f"S{S}/d{d}/{dtype}/{'c' if causal else 'nc'}/{variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_several_query_tiles_and_ragged_tail(variant):
+    """Multi-tile shapes with a tail in both the query and key directions."""
+    for dtype, d, S in ((inputs.BF16, 128, 1000), (inputs.F32, 64, 777), (inputs.BF16, 64, 1541)):
+        for causal in (False, True):
+            p = inputs.make_problem(2, 2, S, d, dtype, causal=causal, seed=S + d)
+            full_check(p, variant, f"B2H2S{S}/d{d}/{dtype}/{'c' if causal else 'nc'}/{variant}")
+
+
+# ---------------------------------------------------------------- invariants through the GPU
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("dtype", [inputs.F32, inputs.BF16])
+def test_identical_value_rows_give_that_row(variant, dtype):
+    torch = torch_cuda()
+    p = inputs.make_problem(1, 2, 300, 64, dtype, causal=True, seed=3)
+    p.v[:] = p.v[:, :1, :]
+    o = run(p, variant).cpu().numpy()
+    want = np.broadcast_to(p.v[:, :1, :].astype(np.float64), o.shape)
+    # a convex combination of identical rows: only the P V rounding remains
+    compare(o, want, dtype, f"identical-rows/{dtype}/{variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_prefix_mean(variant, causal):
+    p = inputs.make_problem(1, 2, 257, 32, inputs.F32, causal=causal, seed=4)
+    p.q[:] = 0
+    o = run(p, variant).cpu().numpy()
+    v = p.v.astype(np.float64)
+    if causal:
+        want = np.cumsum(v, axis=1) / np.arange(1, p.S + 1)[None, :, None]
+    else:
+        want = np.broadcast_to(v.mean(axis=1, keepdims=True), v.shape)
+    compare(o, want, inputs.F32, f"zero-query/{'c' if causal else 'nc'}/{variant}")
+
+
+def test_naive_probability_rows_sum_to_one():
+    torch = torch_cuda()
+    for causal in (False, True):
+        p = inputs.make_problem(1, 2, 333, 64, inputs.BF16, causal=causal, seed=5)
+        need = kb.workspace_size(p.B, p.H, p.S, p.d, dtype="bf16")
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+        run(p, "naive", workspace=ws)
+        P = ws.view(torch.float32).view(p.BH, p.S, p.S).double().cpu().numpy()
+        assert np.all(np.isfinite(P)) and np.all(P >= 0)
+        np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-5)
+        if causal:
+            iu = np.triu_indices(p.S, 1)
+            assert np.all(P[:, iu[0], iu[1]] == 0.0)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_repeat_runs_are_bit_identical(variant):
+    p = inputs.make_problem(2, 4, 700, 128, inputs.BF16, causal=True, seed=6)
+    a = run(p, variant).cpu().numpy()
+    b = run(p, variant).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+def test_variants_agree_with_each_other():
+    p = inputs.make_problem(1, 4, 1024, 64, inputs.F32, causal=True, seed=7)
+    outs = {v: run(p, v).cpu().numpy() for v in VARIANTS}
+    for v in ("naive", "fused"):
+        assert np.max(np.abs(outs[v] - outs["flash"])) <= 2e-5
+
+
+def test_explicit_scale_and_4d_layout():
+    torch = torch_cuda()
+    p = inputs.make_problem(2, 3, 150, 64, inputs.F32, causal=False, seed=8)
+    q, k, v = (t.view(2, 3, 150, 64) for t in to_device(p))
+    for variant in VARIANTS:
+        o = kb.attention(q, k, v, causal=False, variant=variant, scale=0.3)
+        torch.cuda.synchronize()
+        want = oracle.sdpa(p.q, p.k, p.v, causal=False, scale=0.3)
+        compare(o.view(p.BH, p.S, p.d).cpu().numpy(), want, inputs.F32, f"scale0.3/{variant}")
+
+
+# ---------------------------------------------------------------- errors on the device
+
+def test_fused_reports_lds_limit():
+    torch = torch_cuda()
+    info = kb.kb_device_info()
+    S = info["max_lds_per_block"] // 4 + 64
+    q = torch.zeros((1, S, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kb.KbError) as ei:
+        kb.attention(q, q.clone(), q.clone(), variant="fused")
+    assert ei.value.status == 2
+
+
+def test_device_info_is_gfx950():
+    torch_cuda()
+    info = kb.kb_device_info()
+    print(f"[device] {info}", flush=True)
+    assert info["arch"].startswith("gfx950")
+    assert info["compute_units"] > 0

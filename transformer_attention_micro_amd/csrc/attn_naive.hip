@@ -1,0 +1,390 @@
+// attn_naive: the three-pass, bandwidth-bound baseline, for gfx950.
+//
+// Method (kbench page, "The three GPU kernels", the naive kernel): a GEMM
+// writes the full S x S score matrix to DRAM, a row-wise softmax runs over
+// it, and a second GEMM forms P V.  All O(S^2) scores stream through HBM, so
+// the kernel is bound by HBM bandwidth (page section "Expected results").
+//
+// Pass 1  W[bh, i, j] = scale * <Q[bh, i], K[bh, j]>      all i, j < S (fp32)
+// Pass 2  W[bh, i, :] <- softmax over the visible j, in place; masked
+//         entries (causal, j > i) are written as exactly 0
+// Pass 3  O[bh, i, :] = sum_j W[bh, i, j] V[bh, j, :]      fp32 out
+// The full S x S block is computed even under the causal mask: the mask is
+// applied by the softmax pass, as in the plain three-pass reading.
+//
+// bf16 inputs: bf16 MFMA with fp32 accumulate in both GEMMs; pass 3 rounds
+// each fp32 probability to bf16 (round to nearest even) as it loads it, the
+// same rounding the flash kernel applies.  fp32 inputs: fp32 MFMA.
+#include "kb_device.hpp"
+
+using namespace kb;
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------- pass 1 -----
+// Workgroup tile: 128 rows i x 128 columns j; wave w owns rows 32w..32w+31
+// and all four 32-column blocks.  Operands come straight from global memory
+// (both are contiguous along d, the contraction index); C = Q K^T with lane
+// (j % 32) holding one score column, so each store writes 128 contiguous
+// bytes per row.
+template <int D>
+__global__ __launch_bounds__(kThreads) void scores_bf16_kernel(const bf16_t *__restrict__ Q,
+                                                               const bf16_t *__restrict__ K,
+                                                               float *__restrict__ W, int S,
+                                                               float scale) {
+  const int bh = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int i0 = blockIdx.y * 128 + 32 * w;
+  const int j0 = blockIdx.x * 128;
+  const size_t base = (size_t)bh * S * D;
+  const bf16_t *qp = Q + base + (size_t)min(i0 + l32, S - 1) * D + 8 * h;
+  const bf16_t *kp[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) kp[jb] = K + base + (size_t)min(j0 + 32 * jb + l32, S - 1) * D + 8 * h;
+  f32x16 acc[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    const bf16x8 a = *(const bf16x8 *)(qp + 16 * kc);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) acc[jb] = mfma32x16_bf16(a, *(const bf16x8 *)(kp[jb] + 16 * kc), acc[jb]);
+  }
+  float *wp = W + (size_t)bh * S * S;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    const int j = j0 + 32 * jb + l32;
+    if (j >= S) continue;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = i0 + acc_row(v, h);
+      if (i < S) wp[(size_t)i * S + j] = acc[jb][v] * scale;
+    }
+  }
+}
+
+// fp32: contraction step (g, e) uses d-column 8g + 4h + e from lane half h.
+template <int D>
+__global__ __launch_bounds__(kThreads) void scores_f32_kernel(const float *__restrict__ Q,
+                                                              const float *__restrict__ K,
+                                                              float *__restrict__ W, int S,
+                                                              float scale) {
+  const int bh = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int i0 = blockIdx.y * 128 + 32 * w;
+  const int j0 = blockIdx.x * 128;
+  const size_t base = (size_t)bh * S * D;
+  const float *qp = Q + base + (size_t)min(i0 + l32, S - 1) * D + 4 * h;
+  const float *kp[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) kp[jb] = K + base + (size_t)min(j0 + 32 * jb + l32, S - 1) * D + 4 * h;
+  f32x16 acc[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x16{};
+#pragma unroll
+  for (int g = 0; g < D / 8; ++g) {
+    const f32x4 a = *(const f32x4 *)(qp + 8 * g);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const f32x4 b = *(const f32x4 *)(kp[jb] + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[jb] = mfma32x2_f32(a[e], b[e], acc[jb]);
+    }
+  }
+  float *wp = W + (size_t)bh * S * S;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    const int j = j0 + 32 * jb + l32;
+    if (j >= S) continue;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = i0 + acc_row(v, h);
+      if (i < S) wp[(size_t)i * S + j] = acc[jb][v] * scale;
+    }
+  }
+}
+
+// ------------------------------------------------------------- pass 2 -----
+// One workgroup per row.  Vector path: the row (S % 4 == 0, S <= 1024 * NV)
+// is held in registers as NV float4 per thread, so it is read once and
+// written once.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void softmax_vec_kernel(float *__restrict__ W, int S,
+                                                               int causal) {
+  __shared__ float red[kThreads / kWave];
+  const size_t row = blockIdx.x;
+  const int i = (int)(row % (size_t)S);
+  const int nvis = causal ? i + 1 : S;
+  float4 *rp = (float4 *)(W + row * (size_t)S);
+  float4 x[NV];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int e = 4 * (threadIdx.x + kThreads * k);
+    if (e < S) {
+      x[k] = rp[threadIdx.x + kThreads * k];
+      if (e + 0 >= nvis) x[k].x = -INFINITY;
+      if (e + 1 >= nvis) x[k].y = -INFINITY;
+      if (e + 2 >= nvis) x[k].z = -INFINITY;
+      if (e + 3 >= nvis) x[k].w = -INFINITY;
+    } else {
+      x[k] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+    m = fmaxf(m, fmaxf(fmaxf(x[k].x, x[k].y), fmaxf(x[k].z, x[k].w)));
+  }
+  m = block_max<kThreads / kWave>(m, red);
+  float l = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    x[k].x = exp2_fast((x[k].x - m) * kLog2e);
+    x[k].y = exp2_fast((x[k].y - m) * kLog2e);
+    x[k].z = exp2_fast((x[k].z - m) * kLog2e);
+    x[k].w = exp2_fast((x[k].w - m) * kLog2e);
+    l += (x[k].x + x[k].y) + (x[k].z + x[k].w);
+  }
+  l = block_sum<kThreads / kWave>(l, red);
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int e = 4 * (threadIdx.x + kThreads * k);
+    if (e < S)
+      rp[threadIdx.x + kThreads * k] = make_float4(x[k].x * inv, x[k].y * inv, x[k].z * inv, x[k].w * inv);
+  }
+}
+
+// General path (any S): three sweeps over the row in global memory.
+__global__ __launch_bounds__(kThreads) void softmax_any_kernel(float *__restrict__ W, int S, int causal) {
+  __shared__ float red[kThreads / kWave];
+  const size_t row = blockIdx.x;
+  const int i = (int)(row % (size_t)S);
+  const int nvis = causal ? i + 1 : S;
+  float *rp = W + row * (size_t)S;
+  float m = -INFINITY;
+  for (int j = threadIdx.x; j < nvis; j += kThreads) m = fmaxf(m, rp[j]);
+  m = block_max<kThreads / kWave>(m, red);
+  float l = 0.f;
+  for (int j = threadIdx.x; j < nvis; j += kThreads) l += exp2_fast((rp[j] - m) * kLog2e);
+  l = block_sum<kThreads / kWave>(l, red);
+  const float inv = 1.f / l;
+  for (int j = threadIdx.x; j < S; j += kThreads)
+    rp[j] = j < nvis ? exp2_fast((rp[j] - m) * kLog2e) * inv : 0.f;
+}
+
+// ------------------------------------------------------------- pass 3 -----
+// O^T = V^T P^T per workgroup of 128 query rows (wave w: rows 32w..32w+31);
+// 64-key V tiles staged in LDS and read transposed, P^T streamed from global
+// memory.  The key order inside each 16-key chunk matches the transposing
+// read: lane half h holds keys {4h..4h+3, 8+4h..8+4h+3}.
+template <int D, bool VEC>
+__global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float *__restrict__ W,
+                                                           const bf16_t *__restrict__ V,
+                                                           float *__restrict__ O, int S) {
+  constexpr int BC = 64;
+  constexpr int STR = D + 8;
+  constexpr int MB = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int CH = BC * CPR / kThreads;
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[BC * STR];
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int q = blockIdx.x * 128 + 32 * w + l32;
+  const size_t base = (size_t)bh * S * D;
+  const float *prow = W + ((size_t)bh * S + min(q, S - 1)) * (size_t)S;
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  f32x16 oacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
+  for (int kt0 = 0; kt0 < S; kt0 += BC) {
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + c * kThreads;
+      const int row = idx / CPR, col = (idx % CPR) * 8;
+      const int key = kt0 + row;
+      u32x4 val = u32x4{0, 0, 0, 0};
+      if (key < S) val = *(const u32x4 *)(V + base + (size_t)key * D + col);
+      *(u32x4 *)&Vs[row * STR + col] = val;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c16 = 0; c16 < BC / 16; ++c16) {
+      const int k0 = kt0 + 16 * c16 + 4 * h;
+      float pv[8];
+      if (VEC && k0 + 12 <= S) {
+        const float4 a = *(const float4 *)(prow + k0);
+        const float4 b = *(const float4 *)(prow + k0 + 8);
+        pv[0] = a.x; pv[1] = a.y; pv[2] = a.z; pv[3] = a.w;
+        pv[4] = b.x; pv[5] = b.y; pv[6] = b.z; pv[7] = b.w;
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int key = k0 + (s < 4 ? s : 4 + s);
+          pv[s] = key < S ? prow[key] : 0.f;
+        }
+      }
+      bf16x8 pb;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) pb[s] = (bf16_t)pv[s];
+      const bf16_t *vp = &Vs[(16 * c16 + tr_row) * STR + tr_col];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(vp + 32 * mb));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(vp + 8 * STR + 32 * mb));
+        const auto a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[mb] = mfma32x16_bf16(__builtin_bit_cast(bf16x8, a), pb, oacc[mb]);
+      }
+    }
+  }
+  if (q < S) {
+    float *op = O + base + (size_t)q * D + 4 * h;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *(f32x4 *)(op + 32 * mb + 8 * r) =
+            f32x4{oacc[mb][4 * r], oacc[mb][4 * r + 1], oacc[mb][4 * r + 2], oacc[mb][4 * r + 3]};
+  }
+}
+
+// fp32: 32-key V tiles; MFMA step c uses key acc_row(c, h) from lane half h,
+// so a lane reads P[q, 8r + 4h .. 8r + 4h + 3] as one vector for steps 4r..4r+3.
+template <int D, bool VEC>
+__global__ __launch_bounds__(kThreads) void pv_f32_kernel(const float *__restrict__ W,
+                                                          const float *__restrict__ V,
+                                                          float *__restrict__ O, int S) {
+  constexpr int BC = 32;
+  constexpr int STR = D + 4;
+  constexpr int MB = D / 32;
+  constexpr int CPR = D / 4;
+  constexpr int CH = BC * CPR / kThreads;
+  __shared__ __attribute__((aligned(16))) float Vs[BC * STR];
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int q = blockIdx.x * 128 + 32 * w + l32;
+  const size_t base = (size_t)bh * S * D;
+  const float *prow = W + ((size_t)bh * S + min(q, S - 1)) * (size_t)S;
+  f32x16 oacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
+  for (int kt0 = 0; kt0 < S; kt0 += BC) {
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + c * kThreads;
+      const int row = idx / CPR, col = (idx % CPR) * 4;
+      const int key = kt0 + row;
+      f32x4 val = f32x4{};
+      if (key < S) val = *(const f32x4 *)(V + base + (size_t)key * D + col);
+      *(f32x4 *)&Vs[row * STR + col] = val;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int k0 = kt0 + 8 * r + 4 * h;
+      float pv[4];
+      if (VEC && k0 + 4 <= S) {
+        const float4 a = *(const float4 *)(prow + k0);
+        pv[0] = a.x; pv[1] = a.y; pv[2] = a.z; pv[3] = a.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = (k0 + e) < S ? prow[k0 + e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float *vp = &Vs[(8 * r + 4 * h + e) * STR + l32];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb] = mfma32x2_f32(vp[32 * mb], pv[e], oacc[mb]);
+      }
+    }
+  }
+  if (q < S) {
+    float *op = O + base + (size_t)q * D + 4 * h;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *(f32x4 *)(op + 32 * mb + 8 * r) =
+            f32x4{oacc[mb][4 * r], oacc[mb][4 * r + 1], oacc[mb][4 * r + 2], oacc[mb][4 * r + 3]};
+  }
+}
+
+template <int D>
+hipError_t launch_scores(const kb_problem &p) {
+  const int nt = (p.S + 127) / 128;
+  const dim3 grid(nt, nt, p.bh);
+  if (p.bf16)
+    hipLaunchKernelGGL((scores_bf16_kernel<D>), grid, dim3(kThreads), 0, p.stream,
+                       (const bf16_t *)p.Q, (const bf16_t *)p.K, p.work, p.S, p.scale);
+  else
+    hipLaunchKernelGGL((scores_f32_kernel<D>), grid, dim3(kThreads), 0, p.stream,
+                       (const float *)p.Q, (const float *)p.K, p.work, p.S, p.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax(const kb_problem &p) {
+  const size_t rows = (size_t)p.bh * p.S;
+  const dim3 grid((unsigned)rows), block(kThreads);
+  if (p.S % 4 == 0 && p.S <= 1024 * 32) {
+    const int nv = (p.S + 1023) / 1024;
+    if (nv <= 1) hipLaunchKernelGGL(softmax_vec_kernel<1>, grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else if (nv <= 2) hipLaunchKernelGGL(softmax_vec_kernel<2>, grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else if (nv <= 4) hipLaunchKernelGGL(softmax_vec_kernel<4>, grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else if (nv <= 8) hipLaunchKernelGGL(softmax_vec_kernel<8>, grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else if (nv <= 16) hipLaunchKernelGGL(softmax_vec_kernel<16>, grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else hipLaunchKernelGGL(softmax_vec_kernel<32>, grid, block, 0, p.stream, p.work, p.S, p.causal);
+  } else {
+    hipLaunchKernelGGL(softmax_any_kernel, grid, block, 0, p.stream, p.work, p.S, p.causal);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_pv(const kb_problem &p) {
+  const dim3 grid((p.S + 127) / 128, p.bh);
+  const bool vec = p.S % 4 == 0;
+  if (p.bf16) {
+    if (vec)
+      hipLaunchKernelGGL((pv_bf16_kernel<D, true>), grid, dim3(kThreads), 0, p.stream, p.work,
+                         (const bf16_t *)p.V, p.O, p.S);
+    else
+      hipLaunchKernelGGL((pv_bf16_kernel<D, false>), grid, dim3(kThreads), 0, p.stream, p.work,
+                         (const bf16_t *)p.V, p.O, p.S);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((pv_f32_kernel<D, true>), grid, dim3(kThreads), 0, p.stream, p.work,
+                         (const float *)p.V, p.O, p.S);
+    else
+      hipLaunchKernelGGL((pv_f32_kernel<D, false>), grid, dim3(kThreads), 0, p.stream, p.work,
+                         (const float *)p.V, p.O, p.S);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_all(const kb_problem &p) {
+  hipError_t e = launch_scores<D>(p);
+  if (e != hipSuccess) return e;
+  e = launch_softmax(p);
+  if (e != hipSuccess) return e;
+  return launch_pv<D>(p);
+}
+
+}  // namespace
+
+hipError_t kb_launch_naive(const kb_problem &p) {
+  switch (p.D) {
+    case 32: return launch_all<32>(p);
+    case 64: return launch_all<64>(p);
+    case 128: return launch_all<128>(p);
+    default: return hipErrorInvalidValue;
+  }
+}
