@@ -11,8 +11,9 @@ per-launch kernel time used for the roofline fraction.
 
 The JSON line also carries:
   roofline      achieved TFLOP/s per launch vs the MI355X dense bf16 MFMA
-                peak (2516.6 TFLOP/s), and HBM traffic per launch when the
-                --traffic-kib option gives the rocprofv3 counter reading;
+                peak (2516.6 TFLOP/s), and HBM bytes per launch from the
+                rocprofv3 FETCH_SIZE / WRITE_SIZE summary committed under
+                profiles/ (null if the kernel changed since it was taken);
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded,
                 seeded sample of the same workload's query rows (also used
                 to check the GPU output on those rows);
@@ -47,6 +48,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extras", action="store_true", help="skip triad and the naive/fused variants")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, run a plain device copy of this many MiB three times "
+                         "(a kernel of known traffic, used to scale the rocprofv3 byte counters)")
     ap.add_argument("--traffic-kib", type=float, nargs=2, metavar=("FETCH", "WRITE"), default=None,
                     help="rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the flash kernel, "
                          "already scaled by the copy-kernel calibration")
@@ -95,6 +99,22 @@ def cpu_baseline(p, o_gpu, budget_s, seed=1234):
                   f"{t_used:.1f} s; throughput scaled by the rows' algorithmic FLOPs",
         "max_abs_err_vs_gpu_on_sample": max(errs),
     }
+
+
+def measured_traffic(workload):
+    """HBM bytes per flash launch from the committed rocprofv3 counter summary,
+    or None when there is none for this workload or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"flash_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if not sha.startswith(rec["source_sha256_prefix"]):
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def triad_calibration(kb, torch, stream):
@@ -152,7 +172,7 @@ def main():
     kern_ms = float(np.mean(per))
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[p.dtype]
-    traffic = None
+    traffic = measured_traffic(args.workload)
     if args.traffic_kib:
         traffic = int((args.traffic_kib[0] + args.traffic_kib[1]) * 1024)
 
@@ -177,6 +197,16 @@ def main():
                      "kernel_ms_p50": round(float(np.median(per)), 4),
                      "kernel_ms_p99": round(float(np.percentile(per, 99)), 4)},
     }
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": 4 * n, "write": 4 * n}
+        del src, dst
 
     if not args.no_extras:
         extras = {}
