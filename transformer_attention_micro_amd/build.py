@@ -34,7 +34,7 @@ HIPCC_FLAGS = [
 # Extra flags per source.  The flash kernel takes row maxima of MFMA results;
 # without relaxed NaN handling every fmaxf input is first canonicalised (one
 # extra VALU op per score).  Its inputs are finite or -inf, never NaN.
-FILE_FLAGS = {"attn_flash.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"attn_flash.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

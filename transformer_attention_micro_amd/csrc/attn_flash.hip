@@ -88,38 +88,94 @@ struct Swz {
   __device__ static int fv(int r) { return D == 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0; }
 };
 
-// Workgroup of the bf16 kernel: 4 waves x 32 query rows, two workgroups per
-// CU (the two waves sharing a SIMD belong to different workgroups, so their
-// matrix-core and vector phases drift apart and overlap).
-constexpr int kBrB = 128;
+// Workgroup barrier without the memory fence of __syncthreads, which on
+// gfx9 also waits for every outstanding global load, prefetches of later
+// tiles included.  Ordering is explicit instead: LDS reads are drained here
+// (lgkmcnt(0)), direct global->LDS loads are waited for with vmcnt before
+// the call, and the empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt / expcnt untouched
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-// Pipeline per wave, per 64-key tile t.  LDS holds K(t+1) and V(t); the
-// direct loads of K(t+2) and V(t+1) fill the other two buffers and are
-// issued in small groups between the MFMAs instead of in one burst.
-//   A: the MFMAs of S^T(t+1) = K(t+1) Q^T, interleaved with the VALU work
-//      of tile t: row maxima, the rescaling decision and the exponentials;
-//   B: O^T += V(t)^T P(t)^T.
-// The loop is unrolled by two so every LDS buffer is a distinct object and
-// the compiler never waits for loads in flight before an LDS read.
+// Makes `x` depend on `dep` without emitting code: the compiler must
+// produce `dep` first.  Used to keep a register set's new contents from
+// being computed while its old contents are still being read (which would
+// need a second set of registers).
+template <typename T, typename U>
+__device__ __forceinline__ void after(T &x, const U &dep) {
+  asm volatile("" : "+v"(x) : "v"(dep));
+}
+
+// Pins a value in place in the instruction stream (no code): the compiler
+// must compute it before this point and may not move its later uses above.
+template <typename T>
+__device__ __forceinline__ void pin(T &x) {
+  asm volatile("" : "+v"(x));
+}
+
+// bf16 kernel.  A workgroup is 4 waves, one per SIMD, each owning 32 query
+// rows, so it covers 128 queries of one head; its LDS ring (128 KiB) keeps
+// it alone on its CU.  Per 64-key tile step t a wave has three pieces of
+// work:
+//   O^T += V(t-1)^T P(t-1)^T    (MFMA, V from LDS, P from registers)
+//   softmax of tile t           (vector ALU: row max, exponentials, bf16 P)
+//   S^T(t+1) = K(t+1) Q^T       (MFMA, K from LDS)
+// and its instruction stream interleaves them, so the vector ALU works in
+// the shadow of the matrix core (a wave keeps issuing independent
+// instructions while an MFMA runs).  Scores and probabilities live in one
+// set of registers: the MFMAs of P(t-1) V(t-1) read each P block before the
+// softmax overwrites it, and the score MFMAs of each 32-key half of t+1
+// start once the softmax has consumed that half.  When the softmax of t
+// moves the reference maximum, O is rescaled after P(t-1) V(t-1) is in.
+//
+// LDS: rings of kStages K tiles and kStages V tiles filled by direct
+// global->LDS loads; step t issues K(t+4) and V(t+2), and waits (before its
+// barrier) for the loads of step t-3, which hold K(t+1) and V(t-1).
+constexpr int kBrB = 128;
+constexpr int kThreadsB = 256;
+constexpr int kStages = 4;
+
+// s_waitcnt immediate for vmcnt(n), n < 64, other counters left alone.
+constexpr int wait_vm_imm(int n) { return kWaitVm0 | (n & 15) | ((n >> 4) << 14); }
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bf16_kernel(
+__global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1))) void flash_bf16_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
     float *__restrict__ O, int S, int nbh, int nqt, float sl2e) {
-  constexpr int BC = 64;        // keys per tile
-  constexpr int KC = D / 16;    // bf16 MFMA steps along d for S^T
-  constexpr int MB = D / 32;    // 32-row blocks of O^T
-  constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int NCH = BC * CPR; // 16-byte chunks per tile
-  constexpr int CH = NCH / kThreads;  // direct loads per thread per tile and tensor
-  static_assert(CH >= 1 && NCH % kThreads == 0, "tile staging shape");
+  constexpr int BC = 64;                 // keys per tile
+  constexpr int KC = D / 16;             // bf16 MFMA steps along d for S^T
+  constexpr int MB = D / 32;             // 32-row blocks of O^T
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int NW = kThreadsB / 64;     // waves
+  constexpr int NI = BC * CPR / 64;      // 1 KiB direct-load instructions per tile
+  constexpr int CHW = NI / NW;           // of which each wave issues
+  constexpr int NPV = 4 * MB;            // MFMAs of P V per tile
+  constexpr int TB = 2 * BC * D;         // bytes per tile
+  static_assert(NI % NW == 0 && CHW >= 1, "tile staging shape");
   using SW = Swz<D>;
 
-  __shared__ __attribute__((aligned(1024))) bf16_t K0s[BC * D], K1s[BC * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t V0s[BC * D], V1s[BC * D];
+  // One LDS object per stage, so the compiler can tell the buffers being
+  // filled from the ones being read (it would otherwise wait for every load
+  // in flight before each LDS read).  Each is aligned to its size.
+  static_assert(kStages == 4, "the stage ring below is written out for four stages");
+  __shared__ __attribute__((aligned(TB))) bf16_t K0s[BC * D], K1s[BC * D], K2s[BC * D], K3s[BC * D];
+  __shared__ __attribute__((aligned(TB))) bf16_t V0s[BC * D], V1s[BC * D], V2s[BC * D], V3s[BC * D];
+  auto kst = [&](int j) KB_INLINE {
+    return (lds_bf16 *)(j == 0 ? K0s : j == 1 ? K1s : j == 2 ? K2s : K3s);
+  };
+  auto vst = [&](int j) KB_INLINE {
+    return (lds_bf16 *)(j == 0 ? V0s : j == 1 ? V1s : j == 2 ? V2s : V3s);
+  };
 
   int bh, qt;
   if (!tile_of_block(bh, qt, nbh, nqt, CAUSAL)) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wave index is made visibly wave-uniform, so branches on the
+  // wave's tile range stay scalar.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int q0 = qt * kBrB;
   const int qw = q0 + 32 * w;
@@ -136,236 +192,359 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   f32x16 oacc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
-  float m_run, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
   const int kend = CAUSAL ? min(S, q0 + kBrB) : S;
   const int ntiles = (kend + BC - 1) / BC;
   // Tiles this wave computes: causal waves stop after the tile holding
-  // their last query (tiles start at multiples of 64, waves at multiples of
-  // 32, so every computed tile has a visible key for every lane).
+  // their last query.  Query blocks start at multiples of 32 and tiles at
+  // multiples of 64, so every tile before that one is entirely visible to
+  // all 32 queries, and every computed tile has a visible key for each.
   const int tw = CAUSAL ? min(ntiles, (qw + 31) / BC + 1) : ntiles;
-  auto needs_mask = [&](int t) KB_INLINE {
-    const int kt0 = t * BC;
-    return (kt0 + BC > S) || (CAUSAL && kt0 + BC - 1 > qw);
-  };
 
-  // Direct global->LDS loads.  Physical 16-byte slot P of a tile (P = c *
-  // 256 + tid, so each wave instruction fills 1 KiB) holds logical chunk
-  // (P % CPR) ^ f(row) of row P / CPR.  Rows past the end of the sequence
-  // repeat the last row: their scores are masked and their probabilities
-  // are exactly 0, so any finite content is harmless.  A tile index past
-  // the last tile reloads the last tile into a buffer nobody reads, which
-  // keeps the issue code free of branches.
-  uint32_t krow[CH], vrow[CH], kcol[CH], vcol8[CH];
+  // Direct global->LDS loads (buffer loads with the LDS flag).  Instruction
+  // c of a tile fills bytes [1 KiB c, 1 KiB (c + 1)) of the stage; its lane
+  // l writes physical 16-byte slot P = 64 c + l, which holds logical chunk
+  // (P % CPR) ^ f(row) of row P / CPR.  Wave w issues instructions w, w + 4,
+  // ...  The lane's byte offset within a tile is fixed (koff / voff) and the
+  // tile's offset is a scalar, so a load costs no vector instructions.  The
+  // buffer descriptors span this head's K and V exactly: rows past the end
+  // of the sequence, and tiles past the last one, read as zeros (their
+  // scores are masked and their probabilities are exactly 0).  The loads are
+  // issued from inline asm, so their completion is tracked by the explicit
+  // waits of the step loop alone.
+  uint32_t koff[CHW], voff[CHW];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int P = c * kThreads + tid, row = P / CPR;
-    krow[c] = vrow[c] = (uint32_t)row;
-    kcol[c] = (uint32_t)(((P % CPR) ^ SW::fk(row)) * 8);
-    vcol8[c] = (uint32_t)(((P % CPR) ^ SW::fv(row)) * 8);
+  for (int i = 0; i < CHW; ++i) {
+    const int P = 64 * (w + NW * i) + lane, row = P / CPR;
+    koff[i] = (uint32_t)(row * 2 * D + (((P % CPR) ^ SW::fk(row)) << 4));
+    voff[i] = (uint32_t)(row * 2 * D + (((P % CPR) ^ SW::fv(row)) << 4));
   }
-  auto load_chunk = [&](const bf16_t *__restrict__ src, lds_bf16 *dst, int t, int c, bool is_v) KB_INLINE {
-    const int kt0 = min(t, ntiles - 1) * BC;
-    const int row = min((int)krow[c], S - 1 - kt0);
-    const bf16_t *g = src + base + (size_t)kt0 * D + (uint32_t)(row * D) + (is_v ? vcol8[c] : kcol[c]);
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                     (__attribute__((address_space(3))) void *)(dst + (c * kThreads + 64 * w) * 8),
-                                     16, 0, 0);
+  const uint32_t head_bytes = (uint32_t)S * 2u * D;
+  auto rsrc = [&](const bf16_t *p) KB_INLINE {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    u32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r.z = __builtin_amdgcn_readfirstlane(head_bytes);
+    r.w = __builtin_amdgcn_readfirstlane(0x00020000u);  // 32-bit data format, untyped
+    return r;
+  };
+  const u32x4 rk = rsrc(K + base), rv = rsrc(V + base);
+  // Scalar byte offset of tile t (past the last tile: out of range).
+  auto tile_off = [&](int t) KB_INLINE {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(t < ntiles ? (uint32_t)t * BC * 2u * D : head_bytes);
+  };
+  // Load instruction i (0 <= i < CHW) of tile `t` of K (is_v false) or V.
+  auto dma = [&](bool is_v, int i, lds_bf16 *dst, uint32_t toff) KB_INLINE {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + (w + NW * i) * 512));
+    if (is_v)
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :: "s"(m0), "v"(voff[i]), "s"(rv), "s"(toff) : "memory");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :: "s"(m0), "v"(koff[i]), "s"(rk), "s"(toff) : "memory");
+  };
+  auto load_tile = [&](bool is_v, lds_bf16 *dst, int t) KB_INLINE {
+    const uint32_t toff = tile_off(t);
+#pragma unroll
+    for (int i = 0; i < CHW; ++i) dma(is_v, i, dst, toff);
   };
 
-  // K fragment (A operand of S^T) of contraction step kc, key row r.
-  const int fk0 = SW::fk(l32), fk1 = SW::fk(32 + l32);
-  auto kfrag = [&](const lds_bf16 *kb, int half, int kc) KB_INLINE {
-    const int lc = 2 * kc + h;
-    return half ? *(const lds_bf16x8 *)(kb + (32 + l32) * D + ((lc ^ fk1) * 8))
-                : *(const lds_bf16x8 *)(kb + l32 * D + ((lc ^ fk0) * 8));
-  };
-  // Transposing V reads: within each 16-lane group, lane p fetches 4
-  // consecutive d-columns of key row (p / 4); the hardware hands lane i the
-  // 4 keys of column i.  Rows read by this lane: 16 cc + tr_row (+8), all
-  // congruent to tr_row mod 4, hence one swizzle value.
+
+  // LDS operand offsets within a stage (each term stays below the tile
+  // size, and the per-fragment parts are XORs of the swizzled chunk index).
+  //  K fragment (A operand of S^T), contraction step kc, key half `half`:
+  //    row 32 half + l32, logical chunk 2 kc + h, physical chunk
+  //    (2 kc + h) ^ fk(row) (fk is the same for row and row + 32): byte
+  //    offset kx[kc] + half * 64 D with kx[kc] = KL ^ (kc << 5).
+  //  V^T fragment (A operand of O^T, transposing reads): within each 16-lane
+  //    group, lane p fetches 4 consecutive d-columns of key row (p / 4) and
+  //    the hardware hands lane i the 4 keys of column i.  This lane reads key
+  //    rows 16 cc + tr_row (+8), all congruent to tr_row mod 4 (one swizzle
+  //    value fv = 4 g), d-columns 32 mb + tr_col .. +3: byte offset
+  //    vx[mb] + 32 D cc (+ 16 D for the upper 8 rows), vx[mb] = VL ^ (mb << 6).
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  uint32_t vcol[MB];
+  const uint32_t KL = (uint32_t)(l32 * 2 * D + ((h ^ SW::fk(l32)) << 4));
+  const uint32_t VL = (uint32_t)(tr_row * 2 * D + ((SW::fv(tr_row) >> 2) << 6) + ((tr_col >> 3) << 4) +
+                                 (tr_col & 7) * 2);
+  uint32_t kx[KC], vx[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int col = 32 * mb + tr_col;
-    vcol[mb] = (uint32_t)(tr_row * D + (((col >> 3) ^ SW::fv(tr_row)) * 8) + (col & 7));
-  }
+  for (int kc = 0; kc < KC; ++kc) kx[kc] = KL ^ (uint32_t)(kc << 5);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) vx[mb] = VL ^ (uint32_t)(mb << 6);
+  typedef __attribute__((address_space(3))) char lds_char;
+  auto kfrag = [&](const lds_bf16 *kb, int half, int kc) KB_INLINE {
+    return *(const lds_bf16x8 *)((const lds_char *)kb + kx[kc] + half * 64 * D);
+  };
+  // V^T fragment j of a tile: 32-row block mb = j % MB, 16-key chunk j / MB.
   auto vfrag = [&](const lds_bf16 *vb, int j) KB_INLINE {
-    const int mb = j % MB, cc = j / MB;  // cc = 16-key chunk of the tile
-    const lds_bf16 *vr = vb + 16 * cc * D + vcol[mb];
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 8 * D));
+    const int mb = j % MB, cc = j / MB;
+    const lds_char *a = (const lds_char *)vb + vx[mb] + cc * 32 * D;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)a);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a + 16 * D));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // sc[sb]: S^T of the lane's query against the 32 keys of half sb.
+  // Scores of a tile: sc[sb] = S^T of the lane's query against the 32 keys
+  // of half sb (raw dot products).  Probabilities in bf16: pb[cc] =
+  // accumulator slots 8(cc & 1) .. +7 of half cc / 2, i.e. keys
+  // 16 cc + {4h..4h+3, 8+4h..8+4h+3} (the B operand layout of P^T).
   f32x16 sc[2];
-  auto mask_scores = [&](f32x16 *sv, int t) KB_INLINE {
-    // Key offsets beyond `lim` are invisible to this lane's query: past the
-    // sequence end, or (causal) after the query itself.
-    const int lim = (CAUSAL ? min(q, S - 1) : S - 1) - t * BC;
+  bf16x8 pb[4];
+
+  // Scores of the next tile into sc; each half starts once the
+  // probabilities of the old contents (pb[2 half], pb[2 half + 1]) exist.
+  auto qk = [&](const lds_bf16 *kb) KB_INLINE {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (32 * sb + acc_row(v, h) > lim) sv[sb][v] = -INFINITY;
+    for (int kc = 0; kc < KC; ++kc) {
+      bf16x8 a0 = kfrag(kb, 0, kc), a1 = kfrag(kb, 1, kc);
+      if (kc == 0) {
+        after(a0, pb[1]);
+        after(a1, pb[3]);
+      }
+      sc[0] = mfma32x16_bf16(a0, qf[kc], kc == 0 ? f32x16{} : sc[0]);
+      sc[1] = mfma32x16_bf16(a1, qf[kc], kc == 0 ? f32x16{} : sc[1]);
+    }
   };
-  auto row_max = [&](const f32x16 *sv) KB_INLINE {
-    // The scale is positive, so it commutes with max.
+  auto pv = [&](const lds_bf16 *vb) KB_INLINE {
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) oacc[j % MB] = mfma32x16_bf16(vfrag(vb, j), pb[j / MB], oacc[j % MB]);
+  };
+  // Diagonal / ragged tiles: key offsets beyond `lim` are invisible to this
+  // lane's query (past the sequence end, or after the query itself).
+  auto mask = [&](int t) KB_INLINE {
+    const int kt0 = t * BC;
+    if ((kt0 + BC > S) || (CAUSAL && kt0 + BC - 1 > qw)) {
+      const int lim = (CAUSAL ? min(q, S - 1) : S - 1) - kt0;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (32 * sb + acc_row(v, h) > lim) sc[sb][v] = -INFINITY;
+    }
+  };
+  // Softmax, first part: row max and lazy rescaling.  The row max is taken
+  // over the raw dot products (the scale is positive, so it commutes with
+  // max), then in log2 units, with three-input max steps.  The reference
+  // maximum only moves when some row of the wave grows by more than
+  // 2^kRescaleLog2; otherwise the probabilities are taken against the stale
+  // maximum and stay below that bound.  O and l use the same reference, so
+  // O / l is unchanged in exact arithmetic.  The first tile always moves it
+  // (m_run starts at -inf, every row sees a key).  Returns whether it moved;
+  // `alpha` is then the factor for O.
+  auto row_max = [&](float &alpha) KB_INLINE {
     float a = -INFINITY, b = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
-      a = fmaxf(a, fmaxf(sv[0][v], sv[0][v + 1]));
-      b = fmaxf(b, fmaxf(sv[1][v], sv[1][v + 1]));
+      a = fmaxf(fmaxf(a, sc[0][v]), sc[0][v + 1]);
+      b = fmaxf(fmaxf(b, sc[1][v]), sc[1][v + 1]);
     }
-    return xor32_max(fmaxf(a, b)) * sl2e;
+    const float mt = xor32_max(fmaxf(a, b)) * sl2e;
+    const bool grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
+    const float m_new = grow ? fmaxf(m_run, mt) : m_run;
+    alpha = exp2_fast(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+    return grow;
+  };
+  // Softmax, second part, for key half sb: exponentials, bf16 probabilities
+  // (the P operand of P V) and their sum, accumulated from the same rounded
+  // values as the numerator, two per dot-product instruction.
+  auto probs = [&](int sb, float &ls) KB_INLINE {
+    const float nm = -m_run;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[sb][v] = exp2_fast(fmaf(sc[sb][v], sl2e, nm));
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int cc = 2 * sb + c2;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) pb[cc][s2] = (bf16_t)sc[sb][8 * c2 + s2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[cc][2 * e], pb[cc][2 * e + 1]},
+                                            bf16x2{(bf16_t)1.0f, (bf16_t)1.0f}, ls, false);
+    }
   };
 
-  // One pipeline step on tile t, with the direct loads of the next tiles
-  // (kdst <- K(t+2), vdst <- V(t+1)) spread over it.  On entry sc holds
-  // S^T(t), already masked.
-  auto step = [&](int t, const lds_bf16 *knext, const lds_bf16 *vcur, lds_bf16 *kdst, lds_bf16 *vdst) KB_INLINE {
-    // A: S^T(t+1) MFMAs (K fragments read one contraction step ahead),
-    // interleaved with the row maxima, the rescaling decision and the
-    // exponentials of tile t, and with the K(t+2) loads.
-    f32x16 sn[2] = {f32x16{}, f32x16{}};
-    bf16x8 a0 = kfrag(knext, 0, 0), a1 = kfrag(knext, 1, 0);
-    auto qk_step = [&](int kc) KB_INLINE {
-      bf16x8 n0 = a0, n1 = a1;
-      if (kc + 1 < KC) {
-        n0 = kfrag(knext, 0, kc + 1);
-        n1 = kfrag(knext, 1, kc + 1);
-      }
-      sn[0] = mfma32x16_bf16(a0, qf[kc], sn[0]);
-      sn[1] = mfma32x16_bf16(a1, qf[kc], sn[1]);
-      a0 = n0;
-      a1 = n1;
+  // Steady-state step: O += P(t-1) V(t-1), the softmax of t and S^T(t+1) as
+  // one instruction stream of NS slots.  Slot i issues the LDS reads of slot
+  // i + kPre, MFMA i and a share of the vector work, and the compiler may
+  // not move instructions between slots, so the interleave is exactly this:
+  //   MFMA slots  [0, NPV/2)      P V on probability blocks 0-1
+  //               [NPV/2, NPV)    P V on blocks 2-3
+  //               [NPV, NPV+KC)   scores of key half 0 (kc = 0..KC-1)
+  //               [NPV+KC, NS)    scores of key half 1
+  //   vector ops  0..7  row-max steps, 8 finish (m, alpha, l), in the first
+  //               group; 9..32 exponentials and bf16 P of half 0 (writing
+  //               blocks 0-1, already read) in the second; 33..56 those of
+  //               half 1 (blocks 2-3) in the third, ahead of the MFMAs that
+  //               overwrite the half; 57 adds the row sum, in the fourth.
+  auto fused_step = [&](const lds_bf16 *vprev, const lds_bf16 *knext, float &alpha, auto &&ld) KB_INLINE {
+    constexpr int NS = NPV + 2 * KC;
+    constexpr int kPre = 4;
+    constexpr int GA = NPV / 2;
+    auto fetch = [&](int i) KB_INLINE {
+      return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
     };
-    qk_step(0);
-    const float mt = row_max(sc);
-    // Lazy rescaling: the reference maximum only moves when some row of the
-    // wave grows by more than 2^kRescaleLog2; otherwise the probabilities are
-    // taken against the stale maximum and stay below that bound.  O and l use
-    // the same reference, so O / l is unchanged in exact arithmetic.
-    const bool grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
-    const float m_use = fmaxf(m_run, grow ? mt : m_run);
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_use;
-    const float nm = -m_use;
-    // Rescale before the straight-line block below, so the branch does not
-    // split it.
+    // First vector op of slot i (ops are numbered as above).
+    auto op_begin = [](int i) constexpr {
+      return i < GA           ? (9 * i + GA - 1) / GA
+             : i < NPV        ? 9 + (24 * (i - GA) + GA - 1) / GA
+             : i < NPV + KC   ? 33 + (24 * (i - NPV) + KC - 1) / KC
+             : i == NPV + KC  ? 57
+                              : 58;
+    };
+    float a = -INFINITY, b = -INFINITY, nm = 0.f, ls = 0.f;
+    bool grow = false;
+    // Each op pins its inputs and results, so it stays in its slot.
+    auto vop = [&](int k) KB_INLINE {
+      if (k < 8) {
+        pin(a);
+        pin(b);
+        a = fmaxf(fmaxf(a, sc[0][2 * k]), sc[0][2 * k + 1]);
+        b = fmaxf(fmaxf(b, sc[1][2 * k]), sc[1][2 * k + 1]);
+        pin(a);
+        pin(b);
+      } else if (k == 8) {
+        const float mt = xor32_max(fmaxf(a, b)) * sl2e;
+        grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
+        const float m_new = grow ? fmaxf(m_run, mt) : m_run;
+        alpha = exp2_fast(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+        nm = -m_new;
+        pin(nm);
+        pin(l_run);
+      } else if (k < 57) {
+        const int sb = k < 33 ? 0 : 1, r = k - (sb ? 33 : 9);
+        if (r < 16) {
+          float x = sc[sb][r];
+          pin(x);
+          x = exp2_fast(fmaf(x, sl2e, nm));
+          pin(x);
+          sc[sb][r] = x;
+        } else {
+          const int j = r - 16, cc = 2 * sb + j / 4, e = j % 4;
+          bf16x2 pr = {(bf16_t)sc[sb][8 * (j / 4) + 2 * e], (bf16_t)sc[sb][8 * (j / 4) + 2 * e + 1]};
+          pin(pr);
+          pb[cc][2 * e] = pr[0];
+          pb[cc][2 * e + 1] = pr[1];
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(bf16_t)1.0f, (bf16_t)1.0f}, ls, false);
+          pin(ls);
+        }
+      } else if (k == 57) {
+        l_run += ls;
+      }
+    };
+    bf16x8 pbo[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) pbo[cc] = pb[cc];
+    bf16x8 buf[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) buf[i] = fetch(i);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const bf16x8 op = buf[i % kPre];
+      if (i + kPre < NS) buf[i % kPre] = fetch(i + kPre);
+      if (i < NPV) {
+        oacc[i % MB] = mfma32x16_bf16(op, pbo[i / MB], oacc[i % MB]);
+      } else {
+        const int half = (i - NPV) / KC, kc = (i - NPV) % KC;
+        sc[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : sc[half]);
+      }
+#pragma unroll
+      for (int k = op_begin(i); k < op_begin(i + 1); ++k) vop(k);
+      // This step's 2 CHW tile loads, spread evenly over the slots so the
+      // CU's load pipeline never backs up into the instruction stream.
+      constexpr int LDI = NS / (2 * CHW);
+      if (i % LDI == 1 % LDI && i / LDI < 2 * CHW) ld(i / LDI);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return grow;
+  };
+
+
+  // Start of step t: K(t+1) and V(t-1) were loaded in step t-3 (or the
+  // prologue), so wait for this wave's loads up to then; the barrier makes
+  // everyone's resident and ends step t-1 everywhere, freeing K(t) (stage
+  // t % 4) and V(t-2) (stage (t + 2) % 4), which are refilled with K(t+4)
+  // and V(t+2).
+  auto begin_step = [&](int t) KB_INLINE {
+    __builtin_amdgcn_s_waitcnt(wait_vm_imm(4 * CHW));
+    wg_barrier();
+  };
+  auto rescale = [&](bool grow, float alpha) KB_INLINE {
     if (grow) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
     }
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-    constexpr int NST = KC - 1;
-    constexpr int EPS = (32 + NST - 1) / NST;  // exponentials per later step
-#pragma unroll
-    for (int kc = 1; kc < KC; ++kc) {
-      qk_step(kc);
-      if (kc - 1 < CH) load_chunk(K, kdst, t + 2, kc - 1, false);
-#pragma unroll
-      for (int e = 0; e < EPS; ++e) {
-        const int i = (kc - 1) * EPS + e;
-        if (i < 32) {
-          const int sb = i >> 4, v = i & 15;
-          const float p = exp2_fast(fmaf(sc[sb][v], sl2e, nm));
-          sc[sb][v] = p;
-          ls[i & 3] += p;
-        }
-      }
-      if (kc + 1 < KC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next K reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                   // 2 MFMA
-      if (kc - 1 < CH) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 direct load
-      __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS, 0);             // fma, exp, add
+  };
+  // Steady step (1 <= t < tw - 1) with ST = t % 4, so every LDS buffer it
+  // touches is known at compile time.
+  auto steady = [&](auto st_tag, int t) KB_INLINE {
+    constexpr int ST = decltype(st_tag)::value;
+    begin_step(t);
+    const uint32_t tk = tile_off(t + 4), tv = tile_off(t + 2);
+    auto ld = [&](int k) KB_INLINE {
+      if (k < CHW) dma(false, k, kst(ST), tk);
+      else dma(true, k - CHW, vst((ST + 2) % kStages), tv);
+    };
+    float alpha;
+    const bool grow = fused_step(vst((ST + 3) % kStages), kst((ST + 1) % kStages), alpha, ld);
+    rescale(grow, alpha);
+  };
+  // Any step, buffers chosen at run time: the first, the last two of the
+  // wave and the idle steps of causal waves that finished early (each wave
+  // takes part in every step's barrier and loads).
+  auto general = [&](int t) KB_INLINE {
+    const int st = t & 3;
+    begin_step(t);
+    load_tile(false, kst(st), t + 4);
+    load_tile(true, vst((st + 2) & 3), t + 2);
+    float alpha = 1.f;
+    bool grow = false;
+    if (t >= 1 && t - 1 < tw) pv(vst((st + 3) & 3));
+    if (t < tw) {
+      mask(t);
+      grow = row_max(alpha);
+      float ls = 0.f;
+      probs(0, ls);
+      probs(1, ls);
+      l_run += ls;
     }
-    // Loads that did not fit between the MFMAs above.
-#pragma unroll
-    for (int c = KC - 1; c < CH; ++c) load_chunk(K, kdst, t + 2, c, false);
-    l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
-
-    // B: O^T += V^T P^T per 16-key chunk cc (accumulator slots 8c..8c+7 of
-    // key half sb = cc / 2, i.e. keys 16c + {4h..4h+3, 8+4h..8+4h+3}); the
-    // V fragments are read one MFMA ahead, the V(t+1) loads spread between.
-    bf16x8 pb[4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) pb[cc][s] = (bf16_t)sc[cc >> 1][8 * (cc & 1) + s];
-    bf16x8 va = vfrag(vcur, 0);
-    constexpr int NJ = 4 * MB;
-    constexpr int JPL = NJ / CH;  // MFMAs per direct load
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      bf16x8 vn = va;
-      if (j + 1 < NJ) vn = vfrag(vcur, j + 1);
-      oacc[j % MB] = mfma32x16_bf16(va, pb[j / MB], oacc[j % MB]);
-      const bool ld = j % JPL == 0;
-      if (ld) load_chunk(V, vdst, t + 1, j / JPL, true);
-      if (j + 1 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // next V reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                  // MFMA
-      if (ld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);          // direct load
-      va = vn;
-    }
-    if (t + 1 < tw && needs_mask(t + 1)) mask_scores(sn, t + 1);
-    sc[0] = sn[0];
-    sc[1] = sn[1];
-  };
-  // A wave with no tile left to compute still carries its share of the loads.
-  auto loads_only = [&](int t, lds_bf16 *kdst, lds_bf16 *vdst) KB_INLINE {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) load_chunk(K, kdst, t + 2, c, false);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) load_chunk(V, vdst, t + 1, c, true);
+    if (t + 1 < tw) qk(kst((st + 1) & 3));
+    rescale(grow, alpha);
   };
 
-  using T_ = std::integral_constant<bool, true>;
-  using F_ = std::integral_constant<bool, false>;
-  // Iteration t with buffer parity PH = t & 1: LDS holds K(t+1) in
-  // K-buffer !PH and V(t) in V-buffer PH; K(t+2) goes to K-buffer PH (its
-  // K(t) was consumed by the previous iteration) and V(t+1) to V-buffer !PH
-  // (its V(t-1) likewise).
-  auto iteration = [&](auto ph_tag, int t) KB_INLINE {
-    constexpr bool PH = decltype(ph_tag)::value;
-    lds_bf16 *kfree = (lds_bf16 *)(PH ? K1s : K0s);
-    lds_bf16 *knext = (lds_bf16 *)(PH ? K0s : K1s);
-    lds_bf16 *vcur = (lds_bf16 *)(PH ? V1s : V0s);
-    lds_bf16 *vfree = (lds_bf16 *)(PH ? V0s : V1s);
-    if (t < tw) step(t, knext, vcur, kfree, vfree);
-    else loads_only(t, kfree, vfree);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-  };
+  // Prologue: K(0..3), V(0..1); every wave computes S^T(0).
+  load_tile(false, kst(0), 0);
+  load_tile(false, kst(1), 1);
+  load_tile(false, kst(2), 2);
+  load_tile(false, kst(3), 3);
+  load_tile(true, vst(0), 0);
+  load_tile(true, vst(1), 1);
+  __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
+  wg_barrier();
+  qk(kst(0));
 
-  // Prologue: K(0), V(0), K(1); S^T(0) and its maxima, which initialise the
-  // reference maxima.
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    load_chunk(K, (lds_bf16 *)K0s, 0, c, false);
-    load_chunk(V, (lds_bf16 *)V0s, 0, c, true);
-    load_chunk(K, (lds_bf16 *)K1s, 1, c, false);
+  general(0);
+  // Steady steps 1 .. tw - 2: four per iteration, then up to three more.
+  int t = 1;
+  for (; t + 3 <= tw - 2; t += 4) {
+    steady(std::integral_constant<int, 1>{}, t);
+    steady(std::integral_constant<int, 2>{}, t + 1);
+    steady(std::integral_constant<int, 3>{}, t + 2);
+    steady(std::integral_constant<int, 0>{}, t + 3);
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-  sc[0] = sc[1] = f32x16{};
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    const bf16x8 a0 = kfrag((lds_bf16 *)K0s, 0, kc), a1 = kfrag((lds_bf16 *)K0s, 1, kc);
-    sc[0] = mfma32x16_bf16(a0, qf[kc], sc[0]);
-    sc[1] = mfma32x16_bf16(a1, qf[kc], sc[1]);
-  }
-  if (needs_mask(0)) mask_scores(sc, 0);
-  m_run = row_max(sc);
-  // Iteration 0 refills K-buffer 0, which every wave has just read.
-  __syncthreads();
+  if (t <= tw - 2) steady(std::integral_constant<int, 1>{}, t++);
+  if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
+  if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
+  for (; t <= ntiles; ++t) general(t);
 
-  for (int t = 0; t < ntiles; t += 2) {
-    iteration(F_{}, t);
-    if (t + 1 < ntiles) iteration(T_{}, t + 1);
-  }
+  // No tile load may still be writing this workgroup's LDS when it ends.
+  __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
 
   const float inv = 1.f / xor32_sum(l_run);
   if (q < S) {
@@ -531,7 +710,7 @@ hipError_t launch_d(const kb_problem &p) {
   const dim3 grid((unsigned)((total + kXcds - 1) / kXcds * kXcds));
   const float sl2e = p.scale * kLog2e;
   if (p.bf16)
-    hipLaunchKernelGGL((flash_bf16_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, p.stream,
+    hipLaunchKernelGGL((flash_bf16_kernel<D, CAUSAL>), grid, dim3(kThreadsB), 0, p.stream,
                        (const bf16_t *)p.Q, (const bf16_t *)p.K, (const bf16_t *)p.V, p.O, p.S, p.bh,
                        nqt, sl2e);
   else
