@@ -370,17 +370,20 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
 
   // Steady-state step: O += P(t-1) V(t-1), the softmax of t and S^T(t+1) as
   // one instruction stream of NS slots.  Slot i issues the LDS reads of slot
-  // i + kPre, MFMA i and a share of the vector work, and the compiler may
+  // i + kPre, MFMA i and its share of the vector work, and the compiler may
   // not move instructions between slots, so the interleave is exactly this:
-  //   MFMA slots  [0, NPV/2)      P V on probability blocks 0-1
-  //               [NPV/2, NPV)    P V on blocks 2-3
+  //   MFMA slots  [0, GA)         P V on probability blocks 0-1
+  //               [GA, NPV)       P V on blocks 2-3
   //               [NPV, NPV+KC)   scores of key half 0 (kc = 0..KC-1)
   //               [NPV+KC, NS)    scores of key half 1
-  //   vector ops  0..7  row-max steps, 8 finish (m, alpha, l), in the first
-  //               group; 9..32 exponentials and bf16 P of half 0 (writing
-  //               blocks 0-1, already read) in the second; 33..56 those of
-  //               half 1 (blocks 2-3) in the third, ahead of the MFMAs that
-  //               overwrite the half; 57 adds the row sum, in the fourth.
+  //   vector work row-max steps in the first group, finishing in its last
+  //               slot (m, alpha, l); exponentials and bf16 P of key half 0
+  //               (writing blocks 0-1, already read) in the second group;
+  //               those of half 1 (blocks 2-3) in the third, ahead of the
+  //               MFMAs that overwrite each half; the row sum in the fourth.
+  // The exponentials go two values at a time (two fma, two exp) and the
+  // conversion of each pair trails one op behind, so no vector instruction
+  // waits on the one just before it.
   auto fused_step = [&](const lds_bf16 *vprev, const lds_bf16 *knext, float &alpha, auto &&ld) KB_INLINE {
     constexpr int NS = NPV + 2 * KC;
     constexpr int kPre = 4;
@@ -388,53 +391,70 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
     auto fetch = [&](int i) KB_INLINE {
       return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
     };
-    // First vector op of slot i (ops are numbered as above).
-    auto op_begin = [](int i) constexpr {
-      return i < GA           ? (9 * i + GA - 1) / GA
-             : i < NPV        ? 9 + (24 * (i - GA) + GA - 1) / GA
-             : i < NPV + KC   ? 33 + (24 * (i - NPV) + KC - 1) / KC
-             : i == NPV + KC  ? 57
-                              : 58;
-    };
     float a = -INFINITY, b = -INFINITY, nm = 0.f, ls = 0.f;
     bool grow = false;
-    // Each op pins its inputs and results, so it stays in its slot.
-    auto vop = [&](int k) KB_INLINE {
-      if (k < 8) {
-        pin(a);
-        pin(b);
-        a = fmaxf(fmaxf(a, sc[0][2 * k]), sc[0][2 * k + 1]);
-        b = fmaxf(fmaxf(b, sc[1][2 * k]), sc[1][2 * k + 1]);
-        pin(a);
-        pin(b);
-      } else if (k == 8) {
-        const float mt = xor32_max(fmaxf(a, b)) * sl2e;
-        grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
-        const float m_new = grow ? fmaxf(m_run, mt) : m_run;
-        alpha = exp2_fast(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-        nm = -m_new;
-        pin(nm);
-        pin(l_run);
-      } else if (k < 57) {
-        const int sb = k < 33 ? 0 : 1, r = k - (sb ? 33 : 9);
-        if (r < 16) {
-          float x = sc[sb][r];
-          pin(x);
-          x = exp2_fast(fmaf(x, sl2e, nm));
-          pin(x);
-          sc[sb][r] = x;
-        } else {
-          const int j = r - 16, cc = 2 * sb + j / 4, e = j % 4;
-          bf16x2 pr = {(bf16_t)sc[sb][8 * (j / 4) + 2 * e], (bf16_t)sc[sb][8 * (j / 4) + 2 * e + 1]};
-          pin(pr);
-          pb[cc][2 * e] = pr[0];
-          pb[cc][2 * e + 1] = pr[1];
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(bf16_t)1.0f, (bf16_t)1.0f}, ls, false);
-          pin(ls);
-        }
-      } else if (k == 57) {
+    // Row-max step j (0..7): elements 2j, 2j+1 of both halves.
+    auto max_op = [&](int j) KB_INLINE {
+      pin(a);
+      pin(b);
+      a = fmaxf(fmaxf(a, sc[0][2 * j]), sc[0][2 * j + 1]);
+      b = fmaxf(fmaxf(b, sc[1][2 * j]), sc[1][2 * j + 1]);
+      pin(a);
+      pin(b);
+    };
+    auto finish = [&]() KB_INLINE {
+      const float mt = xor32_max(fmaxf(a, b)) * sl2e;
+      grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
+      const float m_new = grow ? fmaxf(m_run, mt) : m_run;
+      alpha = exp2_fast(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      nm = -m_new;
+      pin(nm);
+      pin(l_run);
+    };
+    // bf16 pair p (elements 2p, 2p+1) of half sb -> P and the running sum.
+    auto cvt_pair = [&](int sb, int p) KB_INLINE {
+      bf16x2 pr = {(bf16_t)sc[sb][2 * p], (bf16_t)sc[sb][2 * p + 1]};
+      pin(pr);
+      const int cc = 2 * sb + p / 4, e = p % 4;
+      pb[cc][2 * e] = pr[0];
+      pb[cc][2 * e + 1] = pr[1];
+      ls = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(bf16_t)1.0f, (bf16_t)1.0f}, ls, false);
+      pin(ls);
+    };
+    // Exponential op p (0..8) of half sb: exponentials of pair p (p < 8),
+    // then the conversion of pair p - 1.
+    auto exp_op = [&](int sb, int p) KB_INLINE {
+      if (p < 8) {
+        float x0 = sc[sb][2 * p], x1 = sc[sb][2 * p + 1];
+        pin(x0);
+        pin(x1);
+        x0 = fmaf(x0, sl2e, nm);
+        x1 = fmaf(x1, sl2e, nm);
+        x0 = exp2_fast(x0);
+        x1 = exp2_fast(x1);
+        pin(x0);
+        pin(x1);
+        sc[sb][2 * p] = x0;
+        sc[sb][2 * p + 1] = x1;
+      }
+      if (p > 0) cvt_pair(sb, p - 1);
+    };
+    // Vector work of slot i.  Group sizes: GA slots for the 8 max steps
+    // (finish in the last), GA slots for the 9 ops of half 0, KC slots for
+    // the 9 ops of half 1; op ranges are spread evenly over each group.
+    auto slot_work = [&](int i) KB_INLINE {
+      if (i < GA) {
+        for (int j = (8 * i) / GA; j < (8 * (i + 1)) / GA; ++j) max_op(j);
+        if (i == GA - 1) finish();
+      } else if (i < NPV) {
+        const int g = i - GA;
+        for (int p = (9 * g) / GA; p < (9 * (g + 1)) / GA; ++p) exp_op(0, p);
+      } else if (i < NPV + KC) {
+        const int g = i - NPV;
+        for (int p = (9 * g) / KC; p < (9 * (g + 1)) / KC; ++p) exp_op(1, p);
+      } else if (i == NPV + KC) {
         l_run += ls;
       }
     };
@@ -454,8 +474,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
         const int half = (i - NPV) / KC, kc = (i - NPV) % KC;
         sc[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : sc[half]);
       }
-#pragma unroll
-      for (int k = op_begin(i); k < op_begin(i + 1); ++k) vop(k);
+      slot_work(i);
       // This step's 2 CHW tile loads, spread evenly over the slots so the
       // CU's load pipeline never backs up into the instruction stream.
       constexpr int LDI = NS / (2 * CHW);
