@@ -40,7 +40,7 @@ def nan_output(p):
 
 def sample_rows(S: int, BH: int, seed: int, per_head: int = 64):
     """Flat row ids bh * S + i: tile-edge rows of every head plus seeded rows."""
-    edges = {0, 1, 31, 32, 63, 64, 127, 128, S // 2, S - 2, S - 1}
+    edges = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 511, 512, S // 2, S - 2, S - 1}
     rng = np.random.default_rng(seed)
     rows = []
     for bh in range(BH):

@@ -8,8 +8,9 @@
 // the sequence length.
 //
 // gfx950 design (not the page's scalar design):
-//  * A workgroup is 4 waves; each wave owns 32 query rows, so a workgroup
-//    covers 128 queries of one (batch, head) slice.
+//  * Each wave owns 32 query rows.  bf16: a workgroup is 8 waves (256 queries
+//    of one (batch, head) slice), two per SIMD, alone on its CU; fp32: 4
+//    waves (128 queries).
 //  * Both contractions run on MFMA 32x32 tiles, computed transposed:
 //      S^T = K Q^T   (A = K tile from LDS, B = Q^T kept in VGPRs)
 //      O^T += V^T P^T (A = V^T read from LDS with the transposing ds_read,
@@ -117,9 +118,11 @@ __device__ __forceinline__ void pin(T &x) {
   asm volatile("" : "+v"(x));
 }
 
-// bf16 kernel.  A workgroup is 4 waves, one per SIMD, each owning 32 query
-// rows, so it covers 128 queries of one head; its LDS ring (128 KiB) keeps
-// it alone on its CU.  Per 64-key tile step t a wave has three pieces of
+// bf16 kernel.  A workgroup is 8 waves, two per SIMD, each owning 32 query
+// rows, so it covers 256 queries of one head; its LDS ring (128 KiB) keeps
+// it alone on its CU, and every K/V tile staged there feeds 256 queries.
+// While one wave of a SIMD waits at a barrier or on an LDS read, the other
+// keeps the matrix core busy.  Per 64-key tile step t a wave has three pieces of
 // work:
 //   O^T += V(t-1)^T P(t-1)^T    (MFMA, V from LDS, P from registers)
 //   softmax of tile t           (vector ALU: row max, exponentials, bf16 P)
@@ -135,15 +138,15 @@ __device__ __forceinline__ void pin(T &x) {
 // LDS: rings of kStages K tiles and kStages V tiles filled by direct
 // global->LDS loads; step t issues K(t+4) and V(t+2), and waits (before its
 // barrier) for the loads of step t-3, which hold K(t+1) and V(t-1).
-constexpr int kBrB = 128;
-constexpr int kThreadsB = 256;
+constexpr int kBrB = 256;
+constexpr int kThreadsB = 512;
 constexpr int kStages = 4;
 
 // s_waitcnt immediate for vmcnt(n), n < 64, other counters left alone.
 constexpr int wait_vm_imm(int n) { return kWaitVm0 | (n & 15) | ((n >> 4) << 14); }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1))) void flash_bf16_kernel(
+__global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bf16_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
     float *__restrict__ O, int S, int nbh, int nqt, float sl2e) {
   constexpr int BC = 64;                 // keys per tile
@@ -152,10 +155,10 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int NW = kThreadsB / 64;     // waves
   constexpr int NI = BC * CPR / 64;      // 1 KiB direct-load instructions per tile
-  constexpr int CHW = NI / NW;           // of which each wave issues
+  constexpr int CHW = (NI + NW - 1) / NW;  // of which each wave issues (or none)
   constexpr int NPV = 4 * MB;            // MFMAs of P V per tile
   constexpr int TB = 2 * BC * D;         // bytes per tile
-  static_assert(NI % NW == 0 && CHW >= 1, "tile staging shape");
+  static_assert(CHW >= 1, "tile staging shape");
   using SW = Swz<D>;
 
   // One LDS object per stage, so the compiler can tell the buffers being
@@ -205,9 +208,10 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
   // Direct global->LDS loads (buffer loads with the LDS flag).  Instruction
   // c of a tile fills bytes [1 KiB c, 1 KiB (c + 1)) of the stage; its lane
   // l writes physical 16-byte slot P = 64 c + l, which holds logical chunk
-  // (P % CPR) ^ f(row) of row P / CPR.  Wave w issues instructions w, w + 4,
-  // ...  The lane's byte offset within a tile is fixed (koff / voff) and the
-  // tile's offset is a scalar, so a load costs no vector instructions.  The
+  // (P % CPR) ^ f(row) of row P / CPR.  Wave w issues instructions w, w + 8,
+  // ... (at d = 32 a tile is 4 instructions and waves 4-7 issue none).  The
+  // lane's byte offset within a tile is fixed (koff / voff) and the tile's
+  // offset is a scalar, so a load costs no vector instructions.  The
   // buffer descriptors span this head's K and V exactly: rows past the end
   // of the sequence, and tiles past the last one, read as zeros (their
   // scores are masked and their probabilities are exactly 0).  The loads are
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
   uint32_t koff[CHW], voff[CHW];
 #pragma unroll
   for (int i = 0; i < CHW; ++i) {
-    const int P = 64 * (w + NW * i) + lane, row = P / CPR;
+    const int P = 64 * min(w + NW * i, NI - 1) + lane, row = P / CPR;
     koff[i] = (uint32_t)(row * 2 * D + (((P % CPR) ^ SW::fk(row)) << 4));
     voff[i] = (uint32_t)(row * 2 * D + (((P % CPR) ^ SW::fv(row)) << 4));
   }
@@ -237,6 +241,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
   };
   // Load instruction i (0 <= i < CHW) of tile `t` of K (is_v false) or V.
   auto dma = [&](bool is_v, int i, lds_bf16 *dst, uint32_t toff) KB_INLINE {
+    if (w + NW * i >= NI) return;
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + (w + NW * i) * 512));
     if (is_v)
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
