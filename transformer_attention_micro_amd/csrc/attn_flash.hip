@@ -32,6 +32,7 @@
 //    Heavy (late) query tiles are dispatched first, and blockIdx.x is the
 //    (batch, head) slice, so with round-robin dispatch over the 8 XCDs all
 //    query tiles of a slice share one XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "kb_device.hpp"
@@ -52,24 +53,32 @@ constexpr int kWaitVm0 = 0x0F70;
 #define KB_INLINE __attribute__((always_inline))
 typedef __attribute__((address_space(3))) bf16_t lds_bf16;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;  // MI355X: workgroups are dealt round-robin to 8 XCDs
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Workgroup -> (slice, query tile).  The 1-D grid is padded to a multiple of
-// the XCD count; block L runs on XCD L % 8, so it is given item
-// (L % 8) * per + L / 8 of the (slice-major, query-tile-minor) work list.
-// Each XCD thus owns a contiguous run of slices and works through them one
-// at a time, keeping that slice's K/V hot in its own L2.  Causal: inside a
-// slice the heaviest (last) query tiles come first.  Returns false for the
-// padding blocks.
+// Workgroup -> (slice, query tile).  Block L runs on XCD L % 8 (workgroups
+// are dealt round-robin to the XCDs) as that XCD's k-th workgroup, k = L / 8.
+// XCD x owns the slices [x HP, min(nbh, (x + 1) HP)), HP = ceil(nbh / 8),
+// so every slice's K/V stays in one XCD's L2.  Non-causal: its k-th item
+// is query tile k % nqt of its slice k / nqt (one slice at a time).  Causal:
+// tiles cost work proportional to their index, so the XCD's list runs from
+// the heaviest query tile of each of its slices down to the lightest
+// (longest-processing-time-first order), and the CUs that finish early take
+// the light tiles at the end instead of starting a heavy one late.  Returns
+// false for the padding blocks.
 __device__ __forceinline__ bool tile_of_block(int &bh, int &qt, int nbh, int nqt, bool causal) {
-  const int total = nbh * nqt;
-  const int per = (total + kXcds - 1) / kXcds;
+  const int hp = (nbh + kXcds - 1) / kXcds;
   const int L = blockIdx.x;
-  const int item = (L % kXcds) * per + L / kXcds;
-  if (item >= total) return false;
-  bh = item / nqt;
-  const int t = item % nqt;
-  qt = causal ? nqt - 1 - t : t;
+  const int x = L % kXcds, k = L / kXcds;
+  const int h0 = x * hp;
+  const int hx = min(nbh - h0, hp);  // slices of this XCD (may be <= 0)
+  if (hx <= 0 || k >= hx * nqt) return false;
+  if (causal) {
+    bh = h0 + k % hx;
+    qt = nqt - 1 - k / hx;
+  } else {
+    bh = h0 + k / nqt;
+    qt = k % nqt;
+  }
   return true;
 }
 
@@ -144,6 +153,10 @@ constexpr int kStages = 4;
 
 // s_waitcnt immediate for vmcnt(n), n < 64, other counters left alone.
 constexpr int wait_vm_imm(int n) { return kWaitVm0 | (n & 15) | ((n >> 4) << 14); }
+// ... and lgkmcnt(l), l < 16, as well.
+constexpr int wait_vm_lgkm_imm(int n, int l) { return (wait_vm_imm(n) & ~0x0F00) | ((l & 15) << 8); }
+// Operand fragments each wave reads ahead of its MFMAs.
+constexpr int kPre = 4;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bf16_kernel(
@@ -174,413 +187,467 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     return (lds_bf16 *)(j == 0 ? V0s : j == 1 ? V1s : j == 2 ? V2s : V3s);
   };
 
-  int bh, qt;
-  if (!tile_of_block(bh, qt, nbh, nqt, CAUSAL)) return;
-  // The wave index is made visibly wave-uniform, so branches on the
-  // wave's tile range stay scalar.
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, h = lane >> 5;
-  const int q0 = qt * kBrB;
-  const int qw = q0 + 32 * w;
-  const int q = qw + l32;
-  const size_t base = (size_t)bh * S * D;
+  // Persistent schedule: the grid holds kXcds * nw workgroups (one per CU).
+  // Workgroup g runs on XCD x = g % 8 (workgroups are dealt round-robin to
+  // the XCDs) as its j-th workgroup, j = g / 8.  XCD x owns the slices
+  // [x hp, min(nbh, (x + 1) hp)), hp = ceil(nbh / 8), so each slice's K/V
+  // stays in one XCD's L2, and its workgroups take the XCD's work units
+  // j, j + nw, j + 2 nw, ... (slice-major, so the units in flight share few
+  // slices).  Non-causal, a unit is one query tile.  Causal, query tile t
+  // costs work in proportion to t + 1, so a unit is the pair of tiles
+  // (nqt - 1 - u, u) of one slice (the single middle tile when nqt is odd):
+  // every unit then costs the same and the CUs finish together.
+  const int nw = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jw = blockIdx.x / kXcds;
+  const int hp = (nbh + kXcds - 1) / kXcds, h0 = xcd * hp, hx = min(nbh - h0, hp);
+  const int upd = CAUSAL ? (nqt + 1) / 2 : nqt;  // units per slice
+  bool first_item = true;
+  // One query tile of one slice; every wave of the workgroup calls it with
+  // the same arguments.
+  auto one_item = [&](const int bh, const int qt) KB_INLINE {
+    // The LDS ring of the previous item must be drained by every wave.
+    if (!first_item) wg_barrier();
+    first_item = false;
+    // The wave index is made visibly wave-uniform, so branches on the
+    // wave's tile range stay scalar.
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int q0 = qt * kBrB;
+    const int qw = q0 + 32 * w;
+    const int q = qw + l32;
+    const size_t base = (size_t)bh * S * D;
 
-  bf16x8 qf[KC];
-  {
-    const bf16_t *qp = Q + base + (size_t)min(q, S - 1) * D + 8 * h;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) qf[kc] = *(const bf16x8 *)(qp + 16 * kc);
-  }
+    bf16x8 qf[KC];
+    {
+      const bf16_t *qp = Q + base + (size_t)min(q, S - 1) * D + 8 * h;
+  #pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qf[kc] = *(const bf16x8 *)(qp + 16 * kc);
+    }
 
-  f32x16 oacc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+    f32x16 oacc[MB];
+  #pragma unroll
+    for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
 
-  const int kend = CAUSAL ? min(S, q0 + kBrB) : S;
-  const int ntiles = (kend + BC - 1) / BC;
-  // Tiles this wave computes: causal waves stop after the tile holding
-  // their last query.  Query blocks start at multiples of 32 and tiles at
-  // multiples of 64, so every tile before that one is entirely visible to
-  // all 32 queries, and every computed tile has a visible key for each.
-  const int tw = CAUSAL ? min(ntiles, (qw + 31) / BC + 1) : ntiles;
+    const int kend = CAUSAL ? min(S, q0 + kBrB) : S;
+    const int ntiles = (kend + BC - 1) / BC;
+    // Tiles this wave computes: causal waves stop after the tile holding
+    // their last query.  Query blocks start at multiples of 32 and tiles at
+    // multiples of 64, so every tile before that one is entirely visible to
+    // all 32 queries, and every computed tile has a visible key for each.
+    const int tw = CAUSAL ? min(ntiles, (qw + 31) / BC + 1) : ntiles;
 
-  // Direct global->LDS loads (buffer loads with the LDS flag).  Instruction
-  // c of a tile fills bytes [1 KiB c, 1 KiB (c + 1)) of the stage; its lane
-  // l writes physical 16-byte slot P = 64 c + l, which holds logical chunk
-  // (P % CPR) ^ f(row) of row P / CPR.  Wave w issues instructions w, w + 8,
-  // ... (at d = 32 a tile is 4 instructions and waves 4-7 issue none).  The
-  // lane's byte offset within a tile is fixed (koff / voff) and the tile's
-  // offset is a scalar, so a load costs no vector instructions.  The
-  // buffer descriptors span this head's K and V exactly: rows past the end
-  // of the sequence, and tiles past the last one, read as zeros (their
-  // scores are masked and their probabilities are exactly 0).  The loads are
-  // issued from inline asm, so their completion is tracked by the explicit
-  // waits of the step loop alone.
-  uint32_t koff[CHW], voff[CHW];
-#pragma unroll
-  for (int i = 0; i < CHW; ++i) {
-    const int P = 64 * min(w + NW * i, NI - 1) + lane, row = P / CPR;
-    koff[i] = (uint32_t)(row * 2 * D + (((P % CPR) ^ SW::fk(row)) << 4));
-    voff[i] = (uint32_t)(row * 2 * D + (((P % CPR) ^ SW::fv(row)) << 4));
-  }
-  const uint32_t head_bytes = (uint32_t)S * 2u * D;
-  auto rsrc = [&](const bf16_t *p) KB_INLINE {
-    const uint64_t a = (uint64_t)(uintptr_t)p;
-    u32x4 r;
-    r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
-    r.z = __builtin_amdgcn_readfirstlane(head_bytes);
-    r.w = __builtin_amdgcn_readfirstlane(0x00020000u);  // 32-bit data format, untyped
-    return r;
-  };
-  const u32x4 rk = rsrc(K + base), rv = rsrc(V + base);
-  // Scalar byte offset of tile t (past the last tile: out of range).
-  auto tile_off = [&](int t) KB_INLINE {
-    return (uint32_t)__builtin_amdgcn_readfirstlane(t < ntiles ? (uint32_t)t * BC * 2u * D : head_bytes);
-  };
-  // Load instruction i (0 <= i < CHW) of tile `t` of K (is_v false) or V.
-  auto dma = [&](bool is_v, int i, lds_bf16 *dst, uint32_t toff) KB_INLINE {
-    if (w + NW * i >= NI) return;
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + (w + NW * i) * 512));
-    if (is_v)
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   :: "s"(m0), "v"(voff[i]), "s"(rv), "s"(toff) : "memory");
-    else
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   :: "s"(m0), "v"(koff[i]), "s"(rk), "s"(toff) : "memory");
-  };
-  auto load_tile = [&](bool is_v, lds_bf16 *dst, int t) KB_INLINE {
-    const uint32_t toff = tile_off(t);
-#pragma unroll
-    for (int i = 0; i < CHW; ++i) dma(is_v, i, dst, toff);
-  };
+    // Direct global->LDS loads (buffer loads with the LDS flag).  Instruction
+    // c of a tile fills bytes [1 KiB c, 1 KiB (c + 1)) of the stage; its lane
+    // l writes physical 16-byte slot P = 64 c + l, which holds logical chunk
+    // (P % CPR) ^ f(row) of row P / CPR.  Wave w issues instructions w, w + 8,
+    // ... (at d = 32 a tile is 4 instructions and waves 4-7 issue none).  The
+    // lane's byte offset within a tile is fixed (koff / voff) and the tile's
+    // offset is a scalar, so a load costs no vector instructions.  The
+    // buffer descriptors span this head's K and V exactly: rows past the end
+    // of the sequence, and tiles past the last one, read as zeros (their
+    // scores are masked and their probabilities are exactly 0).  The loads are
+    // issued from inline asm, so their completion is tracked by the explicit
+    // waits of the step loop alone.
+    uint32_t koff[CHW], voff[CHW];
+  #pragma unroll
+    for (int i = 0; i < CHW; ++i) {
+      const int P = 64 * min(w + NW * i, NI - 1) + lane, row = P / CPR;
+      koff[i] = (uint32_t)(row * 2 * D + (((P % CPR) ^ SW::fk(row)) << 4));
+      voff[i] = (uint32_t)(row * 2 * D + (((P % CPR) ^ SW::fv(row)) << 4));
+    }
+    const uint32_t head_bytes = (uint32_t)S * 2u * D;
+    auto rsrc = [&](const bf16_t *p) KB_INLINE {
+      const uint64_t a = (uint64_t)(uintptr_t)p;
+      u32x4 r;
+      r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+      r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+      r.z = __builtin_amdgcn_readfirstlane(head_bytes);
+      r.w = __builtin_amdgcn_readfirstlane(0x00020000u);  // 32-bit data format, untyped
+      return r;
+    };
+    const u32x4 rk = rsrc(K + base), rv = rsrc(V + base);
+    // Scalar byte offset of tile t (past the last tile: out of range).
+    auto tile_off = [&](int t) KB_INLINE {
+      return (uint32_t)__builtin_amdgcn_readfirstlane(t < ntiles ? (uint32_t)t * BC * 2u * D : head_bytes);
+    };
+    // Load instruction i (0 <= i < CHW) of tile `t` of K (is_v false) or V.
+    auto dma = [&](bool is_v, int i, lds_bf16 *dst, uint32_t toff) KB_INLINE {
+      if (w + NW * i >= NI) return;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + (w + NW * i) * 512));
+      if (is_v)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :: "s"(m0), "v"(voff[i]), "s"(rv), "s"(toff) : "memory");
+      else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :: "s"(m0), "v"(koff[i]), "s"(rk), "s"(toff) : "memory");
+    };
+    auto load_tile = [&](bool is_v, lds_bf16 *dst, int t) KB_INLINE {
+      const uint32_t toff = tile_off(t);
+  #pragma unroll
+      for (int i = 0; i < CHW; ++i) dma(is_v, i, dst, toff);
+    };
 
 
-  // LDS operand offsets within a stage (each term stays below the tile
-  // size, and the per-fragment parts are XORs of the swizzled chunk index).
-  //  K fragment (A operand of S^T), contraction step kc, key half `half`:
-  //    row 32 half + l32, logical chunk 2 kc + h, physical chunk
-  //    (2 kc + h) ^ fk(row) (fk is the same for row and row + 32): byte
-  //    offset kx[kc] + half * 64 D with kx[kc] = KL ^ (kc << 5).
-  //  V^T fragment (A operand of O^T, transposing reads): within each 16-lane
-  //    group, lane p fetches 4 consecutive d-columns of key row (p / 4) and
-  //    the hardware hands lane i the 4 keys of column i.  This lane reads key
-  //    rows 16 cc + tr_row (+8), all congruent to tr_row mod 4 (one swizzle
-  //    value fv = 4 g), d-columns 32 mb + tr_col .. +3: byte offset
-  //    vx[mb] + 32 D cc (+ 16 D for the upper 8 rows), vx[mb] = VL ^ (mb << 6).
-  const int tr_row = 4 * h + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const uint32_t KL = (uint32_t)(l32 * 2 * D + ((h ^ SW::fk(l32)) << 4));
-  const uint32_t VL = (uint32_t)(tr_row * 2 * D + ((SW::fv(tr_row) >> 2) << 6) + ((tr_col >> 3) << 4) +
-                                 (tr_col & 7) * 2);
-  uint32_t kx[KC], vx[MB];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) kx[kc] = KL ^ (uint32_t)(kc << 5);
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) vx[mb] = VL ^ (uint32_t)(mb << 6);
-  typedef __attribute__((address_space(3))) char lds_char;
-  auto kfrag = [&](const lds_bf16 *kb, int half, int kc) KB_INLINE {
-    return *(const lds_bf16x8 *)((const lds_char *)kb + kx[kc] + half * 64 * D);
-  };
-  // V^T fragment j of a tile: 32-row block mb = j % MB, 16-key chunk j / MB.
-  auto vfrag = [&](const lds_bf16 *vb, int j) KB_INLINE {
-    const int mb = j % MB, cc = j / MB;
-    const lds_char *a = (const lds_char *)vb + vx[mb] + cc * 32 * D;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)a);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a + 16 * D));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
+    // LDS operand offsets within a stage (each term stays below the tile
+    // size, and the per-fragment parts are XORs of the swizzled chunk index).
+    //  K fragment (A operand of S^T), contraction step kc, key half `half`:
+    //    row 32 half + l32, logical chunk 2 kc + h, physical chunk
+    //    (2 kc + h) ^ fk(row) (fk is the same for row and row + 32): byte
+    //    offset kx[kc] + half * 64 D with kx[kc] = KL ^ (kc << 5).
+    //  V^T fragment (A operand of O^T, transposing reads): within each 16-lane
+    //    group, lane p fetches 4 consecutive d-columns of key row (p / 4) and
+    //    the hardware hands lane i the 4 keys of column i.  This lane reads key
+    //    rows 16 cc + tr_row (+8), all congruent to tr_row mod 4 (one swizzle
+    //    value fv = 4 g), d-columns 32 mb + tr_col .. +3: byte offset
+    //    vx[mb] + 32 D cc (+ 16 D for the upper 8 rows), vx[mb] = VL ^ (mb << 6).
+    const int tr_row = 4 * h + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const uint32_t KL = (uint32_t)(l32 * 2 * D + ((h ^ SW::fk(l32)) << 4));
+    const uint32_t VL = (uint32_t)(tr_row * 2 * D + ((SW::fv(tr_row) >> 2) << 6) + ((tr_col >> 3) << 4) +
+                                   (tr_col & 7) * 2);
+    uint32_t kx[KC], vx[MB];
+  #pragma unroll
+    for (int kc = 0; kc < KC; ++kc) kx[kc] = KL ^ (uint32_t)(kc << 5);
+  #pragma unroll
+    for (int mb = 0; mb < MB; ++mb) vx[mb] = VL ^ (uint32_t)(mb << 6);
+    typedef __attribute__((address_space(3))) char lds_char;
+    auto kfrag = [&](const lds_bf16 *kb, int half, int kc) KB_INLINE {
+      return *(const lds_bf16x8 *)((const lds_char *)kb + kx[kc] + half * 64 * D);
+    };
+    // V^T fragment j of a tile: 32-row block mb = j % MB, 16-key chunk j / MB.
+    auto vfrag = [&](const lds_bf16 *vb, int j) KB_INLINE {
+      const int mb = j % MB, cc = j / MB;
+      const lds_char *a = (const lds_char *)vb + vx[mb] + cc * 32 * D;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)a);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a + 16 * D));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
-  // Scores of a tile: sc[sb] = S^T of the lane's query against the 32 keys
-  // of half sb (raw dot products).  Probabilities in bf16: pb[cc] =
-  // accumulator slots 8(cc & 1) .. +7 of half cc / 2, i.e. keys
-  // 16 cc + {4h..4h+3, 8+4h..8+4h+3} (the B operand layout of P^T).
-  f32x16 sc[2];
-  bf16x8 pb[4];
+    // First fragments of a steady step: V^T of the previous tile (kPre <= 4 MB).
+    auto fetch_first = [&](const lds_bf16 *vb, const lds_bf16 *kb, int i) KB_INLINE {
+      (void)kb;
+      return vfrag(vb, i);
+    };
+    // Operand fragments read ahead of their MFMAs, carried across steps.
+    bf16x8 buf[kPre];
 
-  // Scores of the next tile into sc; each half starts once the
-  // probabilities of the old contents (pb[2 half], pb[2 half + 1]) exist.
-  auto qk = [&](const lds_bf16 *kb) KB_INLINE {
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      bf16x8 a0 = kfrag(kb, 0, kc), a1 = kfrag(kb, 1, kc);
-      if (kc == 0) {
-        after(a0, pb[1]);
-        after(a1, pb[3]);
+    // Scores of a tile: sc[sb] = S^T of the lane's query against the 32 keys
+    // of half sb (raw dot products).  Probabilities in bf16: pb[cc] =
+    // accumulator slots 8(cc & 1) .. +7 of half cc / 2, i.e. keys
+    // 16 cc + {4h..4h+3, 8+4h..8+4h+3} (the B operand layout of P^T).
+    f32x16 sc[2];
+    bf16x8 pb[4];
+
+    // Scores of the next tile into sc; each half starts once the
+    // probabilities of the old contents (pb[2 half], pb[2 half + 1]) exist.
+    auto qk = [&](const lds_bf16 *kb) KB_INLINE {
+  #pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        bf16x8 a0 = kfrag(kb, 0, kc), a1 = kfrag(kb, 1, kc);
+        if (kc == 0) {
+          after(a0, pb[1]);
+          after(a1, pb[3]);
+        }
+        sc[0] = mfma32x16_bf16(a0, qf[kc], kc == 0 ? f32x16{} : sc[0]);
+        sc[1] = mfma32x16_bf16(a1, qf[kc], kc == 0 ? f32x16{} : sc[1]);
       }
-      sc[0] = mfma32x16_bf16(a0, qf[kc], kc == 0 ? f32x16{} : sc[0]);
-      sc[1] = mfma32x16_bf16(a1, qf[kc], kc == 0 ? f32x16{} : sc[1]);
-    }
-  };
-  auto pv = [&](const lds_bf16 *vb) KB_INLINE {
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) oacc[j % MB] = mfma32x16_bf16(vfrag(vb, j), pb[j / MB], oacc[j % MB]);
-  };
-  // Diagonal / ragged tiles: key offsets beyond `lim` are invisible to this
-  // lane's query (past the sequence end, or after the query itself).
-  auto mask = [&](int t) KB_INLINE {
-    const int kt0 = t * BC;
-    if ((kt0 + BC > S) || (CAUSAL && kt0 + BC - 1 > qw)) {
-      const int lim = (CAUSAL ? min(q, S - 1) : S - 1) - kt0;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (32 * sb + acc_row(v, h) > lim) sc[sb][v] = -INFINITY;
-    }
-  };
-  // Softmax, first part: row max and lazy rescaling.  The row max is taken
-  // over the raw dot products (the scale is positive, so it commutes with
-  // max), then in log2 units, with three-input max steps.  The reference
-  // maximum only moves when some row of the wave grows by more than
-  // 2^kRescaleLog2; otherwise the probabilities are taken against the stale
-  // maximum and stay below that bound.  O and l use the same reference, so
-  // O / l is unchanged in exact arithmetic.  The first tile always moves it
-  // (m_run starts at -inf, every row sees a key).  Returns whether it moved;
-  // `alpha` is then the factor for O.
-  auto row_max = [&](float &alpha) KB_INLINE {
-    float a = -INFINITY, b = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      a = fmaxf(fmaxf(a, sc[0][v]), sc[0][v + 1]);
-      b = fmaxf(fmaxf(b, sc[1][v]), sc[1][v + 1]);
-    }
-    const float mt = xor32_max(fmaxf(a, b)) * sl2e;
-    const bool grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
-    const float m_new = grow ? fmaxf(m_run, mt) : m_run;
-    alpha = exp2_fast(m_run - m_new);
-    l_run *= alpha;
-    m_run = m_new;
-    return grow;
-  };
-  // Softmax, second part, for key half sb: exponentials, bf16 probabilities
-  // (the P operand of P V) and their sum, accumulated from the same rounded
-  // values as the numerator, two per dot-product instruction.
-  auto probs = [&](int sb, float &ls) KB_INLINE {
-    const float nm = -m_run;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sc[sb][v] = exp2_fast(fmaf(sc[sb][v], sl2e, nm));
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const int cc = 2 * sb + c2;
-#pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) pb[cc][s2] = (bf16_t)sc[sb][8 * c2 + s2];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[cc][2 * e], pb[cc][2 * e + 1]},
-                                            bf16x2{(bf16_t)1.0f, (bf16_t)1.0f}, ls, false);
-    }
-  };
-
-  // Steady-state step: O += P(t-1) V(t-1), the softmax of t and S^T(t+1) as
-  // one instruction stream of NS slots.  Slot i issues the LDS reads of slot
-  // i + kPre, MFMA i and its share of the vector work, and the compiler may
-  // not move instructions between slots, so the interleave is exactly this:
-  //   MFMA slots  [0, GA)         P V on probability blocks 0-1
-  //               [GA, NPV)       P V on blocks 2-3
-  //               [NPV, NPV+KC)   scores of key half 0 (kc = 0..KC-1)
-  //               [NPV+KC, NS)    scores of key half 1
-  //   vector work row-max steps in the first group, finishing in its last
-  //               slot (m, alpha, l); exponentials and bf16 P of key half 0
-  //               (writing blocks 0-1, already read) in the second group;
-  //               those of half 1 (blocks 2-3) in the third, ahead of the
-  //               MFMAs that overwrite each half; the row sum in the fourth.
-  // The exponentials go two values at a time (two fma, two exp) and the
-  // conversion of each pair trails one op behind, so no vector instruction
-  // waits on the one just before it.
-  auto fused_step = [&](const lds_bf16 *vprev, const lds_bf16 *knext, float &alpha, auto &&ld) KB_INLINE {
-    constexpr int NS = NPV + 2 * KC;
-    constexpr int kPre = 4;
-    constexpr int GA = NPV / 2;
-    auto fetch = [&](int i) KB_INLINE {
-      return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
     };
-    float a = -INFINITY, b = -INFINITY, nm = 0.f, ls = 0.f;
-    bool grow = false;
-    // Row-max step j (0..7): elements 2j, 2j+1 of both halves.
-    auto max_op = [&](int j) KB_INLINE {
-      pin(a);
-      pin(b);
-      a = fmaxf(fmaxf(a, sc[0][2 * j]), sc[0][2 * j + 1]);
-      b = fmaxf(fmaxf(b, sc[1][2 * j]), sc[1][2 * j + 1]);
-      pin(a);
-      pin(b);
+    auto pv = [&](const lds_bf16 *vb) KB_INLINE {
+  #pragma unroll
+      for (int j = 0; j < NPV; ++j) oacc[j % MB] = mfma32x16_bf16(vfrag(vb, j), pb[j / MB], oacc[j % MB]);
     };
-    auto finish = [&]() KB_INLINE {
+    // Diagonal / ragged tiles: key offsets beyond `lim` are invisible to this
+    // lane's query (past the sequence end, or after the query itself).
+    auto mask = [&](int t) KB_INLINE {
+      const int kt0 = t * BC;
+      if ((kt0 + BC > S) || (CAUSAL && kt0 + BC - 1 > qw)) {
+        const int lim = (CAUSAL ? min(q, S - 1) : S - 1) - kt0;
+  #pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (32 * sb + acc_row(v, h) > lim) sc[sb][v] = -INFINITY;
+      }
+    };
+    // Softmax, first part: row max and lazy rescaling.  The row max is taken
+    // over the raw dot products (the scale is positive, so it commutes with
+    // max), then in log2 units, with three-input max steps.  The reference
+    // maximum only moves when some row of the wave grows by more than
+    // 2^kRescaleLog2; otherwise the probabilities are taken against the stale
+    // maximum and stay below that bound.  O and l use the same reference, so
+    // O / l is unchanged in exact arithmetic.  The first tile always moves it
+    // (m_run starts at -inf, every row sees a key).  Returns whether it moved;
+    // `alpha` is then the factor for O.
+    auto row_max = [&](float &alpha) KB_INLINE {
+      float a = -INFINITY, b = -INFINITY;
+  #pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        a = fmaxf(fmaxf(a, sc[0][v]), sc[0][v + 1]);
+        b = fmaxf(fmaxf(b, sc[1][v]), sc[1][v + 1]);
+      }
       const float mt = xor32_max(fmaxf(a, b)) * sl2e;
-      grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
+      const bool grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
       const float m_new = grow ? fmaxf(m_run, mt) : m_run;
       alpha = exp2_fast(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
-      nm = -m_new;
-      pin(nm);
-      pin(l_run);
+      return grow;
     };
-    // bf16 pair p (elements 2p, 2p+1) of half sb -> P and the running sum.
-    auto cvt_pair = [&](int sb, int p) KB_INLINE {
-      bf16x2 pr = {(bf16_t)sc[sb][2 * p], (bf16_t)sc[sb][2 * p + 1]};
-      pin(pr);
-      const int cc = 2 * sb + p / 4, e = p % 4;
-      pb[cc][2 * e] = pr[0];
-      pb[cc][2 * e + 1] = pr[1];
-      ls = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(bf16_t)1.0f, (bf16_t)1.0f}, ls, false);
-      pin(ls);
-    };
-    // Exponential op p (0..8) of half sb: exponentials of pair p (p < 8),
-    // then the conversion of pair p - 1.
-    auto exp_op = [&](int sb, int p) KB_INLINE {
-      if (p < 8) {
-        float x0 = sc[sb][2 * p], x1 = sc[sb][2 * p + 1];
-        pin(x0);
-        pin(x1);
-        x0 = fmaf(x0, sl2e, nm);
-        x1 = fmaf(x1, sl2e, nm);
-        x0 = exp2_fast(x0);
-        x1 = exp2_fast(x1);
-        pin(x0);
-        pin(x1);
-        sc[sb][2 * p] = x0;
-        sc[sb][2 * p + 1] = x1;
+    // Softmax, second part, for key half sb: exponentials, bf16 probabilities
+    // (the P operand of P V) and their fp32 sum.  The sum uses plain adds: the
+    // packed dot-product instruction would run on the matrix pipeline and
+    // delay the MFMAs.
+    auto probs = [&](int sb, float &ls) KB_INLINE {
+      const float nm = -m_run;
+  #pragma unroll
+      for (int v = 0; v < 16; ++v) sc[sb][v] = exp2_fast(fmaf(sc[sb][v], sl2e, nm));
+      float s0 = 0.f, s1 = 0.f;
+  #pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        s0 += sc[sb][v];
+        s1 += sc[sb][v + 1];
       }
-      if (p > 0) cvt_pair(sb, p - 1);
+      ls += s0 + s1;
+  #pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int cc = 2 * sb + c2;
+  #pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) pb[cc][s2] = (bf16_t)sc[sb][8 * c2 + s2];
+      }
     };
-    // Vector work of slot i.  Group sizes: GA slots for the 8 max steps
-    // (finish in the last), GA slots for the 9 ops of half 0, KC slots for
-    // the 9 ops of half 1; op ranges are spread evenly over each group.
-    auto slot_work = [&](int i) KB_INLINE {
-      if (i < GA) {
-        for (int j = (8 * i) / GA; j < (8 * (i + 1)) / GA; ++j) max_op(j);
-        if (i == GA - 1) finish();
-      } else if (i < NPV) {
-        const int g = i - GA;
-        for (int p = (9 * g) / GA; p < (9 * (g + 1)) / GA; ++p) exp_op(0, p);
-      } else if (i < NPV + KC) {
-        const int g = i - NPV;
-        for (int p = (9 * g) / KC; p < (9 * (g + 1)) / KC; ++p) exp_op(1, p);
-      } else if (i == NPV + KC) {
+
+    // Steady-state step: O += P(t-1) V(t-1), the softmax of t and S^T(t+1) as
+    // one instruction stream of NS slots.  Slot i issues the LDS reads of slot
+    // i + kPre, MFMA i and its share of the vector work, and the compiler may
+    // not move instructions between slots, so the interleave is exactly this:
+    //   MFMA slots  [0, GA)         P V on probability blocks 0-1
+    //               [GA, NPV)       P V on blocks 2-3
+    //               [NPV, NPV+KC)   scores of key half 0 (kc = 0..KC-1)
+    //               [NPV+KC, NS)    scores of key half 1
+    //   vector work row-max steps in the first group, finishing in its last
+    //               slot (m, alpha, l); exponentials and bf16 P of key half 0
+    //               (writing blocks 0-1, already read) in the second group;
+    //               those of half 1 (blocks 2-3) in the third, ahead of the
+    //               MFMAs that overwrite each half; the row sum in the fourth.
+    // The exponentials go two values at a time (two fma, two exp) and the
+    // conversion of each pair trails one op behind, so no vector instruction
+    // waits on the one just before it.
+    auto fused_step = [&](const lds_bf16 *vprev, const lds_bf16 *knext, const lds_bf16 *vnn,
+                          const lds_bf16 *knn, float &alpha, auto &&ld) KB_INLINE {
+      constexpr int NS = NPV + 2 * KC;
+      constexpr int GA = NPV / 2;
+      static_assert(NS % kPre == 0 && NPV >= kPre, "fragment ring");
+      // Fragment i of this step (i < NS) or of the next one (i >= NS, read
+      // from the next step's stages, resident since this step's barrier).
+      auto fetch = [&](int i) KB_INLINE {
+        if (i >= NS) return fetch_first(vnn, knn, i - NS);
+        return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
+      };
+      float a = -INFINITY, b = -INFINITY, nm = 0.f, ls = 0.f, ls2 = 0.f;
+      bool grow = false;
+      // Row-max step j (0..7): elements 2j, 2j+1 of both halves.
+      auto max_op = [&](int j) KB_INLINE {
+        pin(a);
+        pin(b);
+        a = fmaxf(fmaxf(a, sc[0][2 * j]), sc[0][2 * j + 1]);
+        b = fmaxf(fmaxf(b, sc[1][2 * j]), sc[1][2 * j + 1]);
+        pin(a);
+        pin(b);
+      };
+      auto finish = [&]() KB_INLINE {
+        const float mt = xor32_max(fmaxf(a, b)) * sl2e;
+        grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
+        const float m_new = grow ? fmaxf(m_run, mt) : m_run;
+        alpha = exp2_fast(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+        nm = -m_new;
+        pin(nm);
+        pin(l_run);
+      };
+      // bf16 pair p (elements 2p, 2p+1) of half sb -> P, and the pair into the
+      // two running sums (plain adds: the packed dot product would occupy the
+      // matrix pipeline).
+      auto cvt_pair = [&](int sb, int p) KB_INLINE {
+        bf16x2 pr = {(bf16_t)sc[sb][2 * p], (bf16_t)sc[sb][2 * p + 1]};
+        pin(pr);
+        const int cc = 2 * sb + p / 4, e = p % 4;
+        pb[cc][2 * e] = pr[0];
+        pb[cc][2 * e + 1] = pr[1];
+        ls += sc[sb][2 * p];
+        ls2 += sc[sb][2 * p + 1];
+        pin(ls);
+        pin(ls2);
+      };
+      // Exponential op p (0..8) of half sb: exponentials of pair p (p < 8),
+      // then the conversion of pair p - 1.
+      auto exp_op = [&](int sb, int p) KB_INLINE {
+        if (p < 8) {
+          float x0 = sc[sb][2 * p], x1 = sc[sb][2 * p + 1];
+          pin(x0);
+          pin(x1);
+          x0 = fmaf(x0, sl2e, nm);
+          x1 = fmaf(x1, sl2e, nm);
+          x0 = exp2_fast(x0);
+          x1 = exp2_fast(x1);
+          pin(x0);
+          pin(x1);
+          sc[sb][2 * p] = x0;
+          sc[sb][2 * p + 1] = x1;
+        }
+        if (p > 0) cvt_pair(sb, p - 1);
+      };
+      // Vector work of slot i.  Group sizes: GA slots for the 8 max steps
+      // (finish in the last), GA slots for the 9 ops of half 0, KC slots for
+      // the 9 ops of half 1; op ranges are spread evenly over each group.
+      auto slot_work = [&](int i) KB_INLINE {
+        if (i < GA) {
+          for (int j = (8 * i) / GA; j < (8 * (i + 1)) / GA; ++j) max_op(j);
+          if (i == GA - 1) finish();
+        } else if (i < NPV) {
+          const int g = i - GA;
+          for (int p = (9 * g) / GA; p < (9 * (g + 1)) / GA; ++p) exp_op(0, p);
+        } else if (i < NPV + KC) {
+          const int g = i - NPV;
+          for (int p = (9 * g) / KC; p < (9 * (g + 1)) / KC; ++p) exp_op(1, p);
+        } else if (i == NPV + KC) {
+          l_run += ls + ls2;
+        }
+      };
+      bf16x8 pbo[4];
+  #pragma unroll
+      for (int cc = 0; cc < 4; ++cc) pbo[cc] = pb[cc];
+  #pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const bf16x8 op = buf[i % kPre];
+        buf[i % kPre] = fetch(i + kPre);
+        if (i < NPV) {
+          oacc[i % MB] = mfma32x16_bf16(op, pbo[i / MB], oacc[i % MB]);
+        } else {
+          const int half = (i - NPV) / KC, kc = (i - NPV) % KC;
+          sc[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : sc[half]);
+        }
+        slot_work(i);
+        // This step's 2 CHW tile loads, spread evenly over the slots so the
+        // CU's load pipeline never backs up into the instruction stream.
+        constexpr int LDI = NS / (2 * CHW);
+        if (i % LDI == 1 % LDI && i / LDI < 2 * CHW) ld(i / LDI);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return grow;
+    };
+
+
+    // Start of step t: wait for this wave's loads of step t-2 (K(t+2), V(t))
+    // and earlier, and for its LDS reads except the last 2 kPre
+    // instructions (the next step's first fragments, read ahead from stages
+    // nobody refills in step t).  The barrier then makes everyone's loads
+    // resident and ends step t-1's reads everywhere, freeing K(t) (stage
+    // t % 4) and V(t-2) (stage (t + 2) % 4), which are refilled with K(t+4)
+    // and V(t+2); K(t+2) and V(t) are now readable, so the end of step t
+    // reads the first fragments of step t+1 from them.
+    auto begin_step = [&](int t) KB_INLINE {
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm_imm(2 * CHW, 2 * kPre));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    auto rescale = [&](bool grow, float alpha) KB_INLINE {
+      if (grow) {
+  #pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+      }
+    };
+    // Steady step (1 <= t < tw - 1) with ST = t % 4, so every LDS buffer it
+    // touches is known at compile time.
+    auto steady = [&](auto st_tag, int t) KB_INLINE {
+      constexpr int ST = decltype(st_tag)::value;
+      begin_step(t);
+      const uint32_t tk = tile_off(t + 4), tv = tile_off(t + 2);
+      auto ld = [&](int k) KB_INLINE {
+        if (k < CHW) dma(false, k, kst(ST), tk);
+        else dma(true, k - CHW, vst((ST + 2) % kStages), tv);
+      };
+      float alpha;
+      const bool grow = fused_step(vst((ST + 3) % kStages), kst((ST + 1) % kStages), vst(ST),
+                                   kst((ST + 2) % kStages), alpha, ld);
+      rescale(grow, alpha);
+    };
+    // Any step, buffers chosen at run time: the first, the last two of the
+    // wave and the idle steps of causal waves that finished early (each wave
+    // takes part in every step's barrier and loads).
+    auto general = [&](int t) KB_INLINE {
+      const int st = t & 3;
+      begin_step(t);
+      load_tile(false, kst(st), t + 4);
+      load_tile(true, vst((st + 2) & 3), t + 2);
+      float alpha = 1.f;
+      bool grow = false;
+      if (t >= 1 && t - 1 < tw) pv(vst((st + 3) & 3));
+      if (t < tw) {
+        mask(t);
+        grow = row_max(alpha);
+        float ls = 0.f;
+        probs(0, ls);
+        probs(1, ls);
         l_run += ls;
       }
+      if (t + 1 < tw) qk(kst((st + 1) & 3));
+      rescale(grow, alpha);
     };
-    bf16x8 pbo[4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) pbo[cc] = pb[cc];
-    bf16x8 buf[kPre];
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) buf[i] = fetch(i);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const bf16x8 op = buf[i % kPre];
-      if (i + kPre < NS) buf[i % kPre] = fetch(i + kPre);
-      if (i < NPV) {
-        oacc[i % MB] = mfma32x16_bf16(op, pbo[i / MB], oacc[i % MB]);
-      } else {
-        const int half = (i - NPV) / KC, kc = (i - NPV) % KC;
-        sc[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : sc[half]);
-      }
-      slot_work(i);
-      // This step's 2 CHW tile loads, spread evenly over the slots so the
-      // CU's load pipeline never backs up into the instruction stream.
-      constexpr int LDI = NS / (2 * CHW);
-      if (i % LDI == 1 % LDI && i / LDI < 2 * CHW) ld(i / LDI);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return grow;
-  };
 
-
-  // Start of step t: K(t+1) and V(t-1) were loaded in step t-3 (or the
-  // prologue), so wait for this wave's loads up to then; the barrier makes
-  // everyone's resident and ends step t-1 everywhere, freeing K(t) (stage
-  // t % 4) and V(t-2) (stage (t + 2) % 4), which are refilled with K(t+4)
-  // and V(t+2).
-  auto begin_step = [&](int t) KB_INLINE {
-    __builtin_amdgcn_s_waitcnt(wait_vm_imm(4 * CHW));
+    // Prologue: K(0..3), V(0..1); every wave computes S^T(0).
+    load_tile(false, kst(0), 0);
+    load_tile(false, kst(1), 1);
+    load_tile(false, kst(2), 2);
+    load_tile(false, kst(3), 3);
+    load_tile(true, vst(0), 0);
+    load_tile(true, vst(1), 1);
+    __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
     wg_barrier();
-  };
-  auto rescale = [&](bool grow, float alpha) KB_INLINE {
-    if (grow) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+    qk(kst(0));
+
+    general(0);
+    // Steady steps 1 .. tw - 2: four per iteration, then up to three more.
+    // The first fragments of step 1 are V(0) (stage 0), read ahead here.
+    int t = 1;
+  #pragma unroll
+    for (int i = 0; i < kPre; ++i) buf[i] = fetch_first(vst(0), kst(2), i);
+    for (; t + 3 <= tw - 2; t += 4) {
+      steady(std::integral_constant<int, 1>{}, t);
+      steady(std::integral_constant<int, 2>{}, t + 1);
+      steady(std::integral_constant<int, 3>{}, t + 2);
+      steady(std::integral_constant<int, 0>{}, t + 3);
+    }
+    if (t <= tw - 2) steady(std::integral_constant<int, 1>{}, t++);
+    if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
+    if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
+    for (; t <= ntiles; ++t) general(t);
+
+    // No tile load may still be writing this workgroup's LDS when it ends.
+    __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
+
+    const float inv = 1.f / xor32_sum(l_run);
+    if (q < S) {
+      float *op = O + base + (size_t)q * D + 4 * h;
+  #pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 o4 = {oacc[mb][4 * r] * inv, oacc[mb][4 * r + 1] * inv,
+                            oacc[mb][4 * r + 2] * inv, oacc[mb][4 * r + 3] * inv};
+          *(f32x4 *)(op + 32 * mb + 8 * r) = o4;
+        }
     }
   };
-  // Steady step (1 <= t < tw - 1) with ST = t % 4, so every LDS buffer it
-  // touches is known at compile time.
-  auto steady = [&](auto st_tag, int t) KB_INLINE {
-    constexpr int ST = decltype(st_tag)::value;
-    begin_step(t);
-    const uint32_t tk = tile_off(t + 4), tv = tile_off(t + 2);
-    auto ld = [&](int k) KB_INLINE {
-      if (k < CHW) dma(false, k, kst(ST), tk);
-      else dma(true, k - CHW, vst((ST + 2) % kStages), tv);
-    };
-    float alpha;
-    const bool grow = fused_step(vst((ST + 3) % kStages), kst((ST + 1) % kStages), alpha, ld);
-    rescale(grow, alpha);
-  };
-  // Any step, buffers chosen at run time: the first, the last two of the
-  // wave and the idle steps of causal waves that finished early (each wave
-  // takes part in every step's barrier and loads).
-  auto general = [&](int t) KB_INLINE {
-    const int st = t & 3;
-    begin_step(t);
-    load_tile(false, kst(st), t + 4);
-    load_tile(true, vst((st + 2) & 3), t + 2);
-    float alpha = 1.f;
-    bool grow = false;
-    if (t >= 1 && t - 1 < tw) pv(vst((st + 3) & 3));
-    if (t < tw) {
-      mask(t);
-      grow = row_max(alpha);
-      float ls = 0.f;
-      probs(0, ls);
-      probs(1, ls);
-      l_run += ls;
+  for (int u = jw; u < hx * upd; u += nw) {
+    const int bh = h0 + u / upd, r = u % upd;
+    if (CAUSAL) {
+      one_item(bh, nqt - 1 - r);
+      if (r != nqt - 1 - r) one_item(bh, r);
+    } else {
+      one_item(bh, r);
     }
-    if (t + 1 < tw) qk(kst((st + 1) & 3));
-    rescale(grow, alpha);
-  };
-
-  // Prologue: K(0..3), V(0..1); every wave computes S^T(0).
-  load_tile(false, kst(0), 0);
-  load_tile(false, kst(1), 1);
-  load_tile(false, kst(2), 2);
-  load_tile(false, kst(3), 3);
-  load_tile(true, vst(0), 0);
-  load_tile(true, vst(1), 1);
-  __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
-  wg_barrier();
-  qk(kst(0));
-
-  general(0);
-  // Steady steps 1 .. tw - 2: four per iteration, then up to three more.
-  int t = 1;
-  for (; t + 3 <= tw - 2; t += 4) {
-    steady(std::integral_constant<int, 1>{}, t);
-    steady(std::integral_constant<int, 2>{}, t + 1);
-    steady(std::integral_constant<int, 3>{}, t + 2);
-    steady(std::integral_constant<int, 0>{}, t + 3);
-  }
-  if (t <= tw - 2) steady(std::integral_constant<int, 1>{}, t++);
-  if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
-  if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
-  for (; t <= ntiles; ++t) general(t);
-
-  // No tile load may still be writing this workgroup's LDS when it ends.
-  __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
-
-  const float inv = 1.f / xor32_sum(l_run);
-  if (q < S) {
-    float *op = O + base + (size_t)q * D + 4 * h;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f32x4 o4 = {oacc[mb][4 * r] * inv, oacc[mb][4 * r + 1] * inv,
-                          oacc[mb][4 * r + 2] * inv, oacc[mb][4 * r + 3] * inv};
-        *(f32x4 *)(op + 32 * mb + 8 * r) = o4;
-      }
   }
 }
 
@@ -725,16 +792,38 @@ __global__ __launch_bounds__(kThreads) void flash_f32_kernel(const float *__rest
   }
 }
 
+// Work units per slice of the persistent bf16 schedule.
+constexpr int causal_units(int nqt, bool causal) { return causal ? (nqt + 1) / 2 : nqt; }
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_d(const kb_problem &p) {
   const int br = p.bf16 ? kBrB : kBr;
   const int nqt = (p.S + br - 1) / br;
-  const long long total = (long long)p.bh * nqt;
-  if (total > 0x7fffffffLL - kXcds) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((total + kXcds - 1) / kXcds * kXcds));
+  // kXcds workgroups per item of the longest per-XCD list (see tile_of_block).
+  const long long per = (long long)((p.bh + kXcds - 1) / kXcds) * nqt;
+  if (per * kXcds > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(per * kXcds));
+  // bf16: persistent, one workgroup per CU at most, kXcds * nw in all (see
+  // the kernel's schedule), never more than there are work units.
+  const long long units = (long long)((p.bh + kXcds - 1) / kXcds) * (causal_units(nqt, CAUSAL));
+  const int nw = (int)std::max(1LL, std::min<long long>(units, std::max(1, cu_count() / kXcds)));
+  const dim3 grid_b((unsigned)(nw * kXcds));
   const float sl2e = p.scale * kLog2e;
   if (p.bf16)
-    hipLaunchKernelGGL((flash_bf16_kernel<D, CAUSAL>), grid, dim3(kThreadsB), 0, p.stream,
+    hipLaunchKernelGGL((flash_bf16_kernel<D, CAUSAL>), grid_b, dim3(kThreadsB), 0, p.stream,
                        (const bf16_t *)p.Q, (const bf16_t *)p.K, (const bf16_t *)p.V, p.O, p.S, p.bh,
                        nqt, sl2e);
   else
