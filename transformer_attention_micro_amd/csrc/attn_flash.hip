@@ -174,18 +174,10 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
   static_assert(CHW >= 1, "tile staging shape");
   using SW = Swz<D>;
 
-  // One LDS object per stage, so the compiler can tell the buffers being
-  // filled from the ones being read (it would otherwise wait for every load
-  // in flight before each LDS read).  Each is aligned to its size.
-  static_assert(kStages == 4, "the stage ring below is written out for four stages");
-  __shared__ __attribute__((aligned(TB))) bf16_t K0s[BC * D], K1s[BC * D], K2s[BC * D], K3s[BC * D];
-  __shared__ __attribute__((aligned(TB))) bf16_t V0s[BC * D], V1s[BC * D], V2s[BC * D], V3s[BC * D];
-  auto kst = [&](int j) KB_INLINE {
-    return (lds_bf16 *)(j == 0 ? K0s : j == 1 ? K1s : j == 2 ? K2s : K3s);
-  };
-  auto vst = [&](int j) KB_INLINE {
-    return (lds_bf16 *)(j == 0 ? V0s : j == 1 ? V1s : j == 2 ? V2s : V3s);
-  };
+  // The LDS ring: kStages K tiles, then kStages V tiles, each BC x D.
+  __shared__ __attribute__((aligned(TB))) bf16_t ring[2 * kStages * BC * D];
+  auto kst = [&](int j) KB_INLINE { return (lds_bf16 *)(ring + j * BC * D); };
+  auto vst = [&](int j) KB_INLINE { return (lds_bf16 *)(ring + (kStages + j) * BC * D); };
 
   // Persistent schedule: the grid holds kXcds * nw workgroups (one per CU).
   // Workgroup g runs on XCD x = g % 8 (workgroups are dealt round-robin to
@@ -305,19 +297,33 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     const uint32_t KL = (uint32_t)(l32 * 2 * D + ((h ^ SW::fk(l32)) << 4));
     const uint32_t VL = (uint32_t)(tr_row * 2 * D + ((SW::fv(tr_row) >> 2) << 6) + ((tr_col >> 3) << 4) +
                                    (tr_col & 7) * 2);
+    // Per-lane LDS addresses of the fragments in stage 0 of each ring (kx,
+    // vx), made opaque to the compiler: every fragment address is then one
+    // of these plus a constant below 64 KiB (stage, key half or 16-key
+    // chunk), which the LDS instruction takes as its immediate offset.
+    typedef __attribute__((address_space(3))) char lds_char;
+    const uint32_t k_ring = (uint32_t)(uintptr_t)(const lds_char *)kst(0);
+    const uint32_t v_ring = (uint32_t)(uintptr_t)(const lds_char *)vst(0);
     uint32_t kx[KC], vx[MB];
   #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) kx[kc] = KL ^ (uint32_t)(kc << 5);
+    for (int kc = 0; kc < KC; ++kc) {
+      kx[kc] = k_ring + (KL ^ (uint32_t)(kc << 5));
+      pin(kx[kc]);
+    }
   #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) vx[mb] = VL ^ (uint32_t)(mb << 6);
-    typedef __attribute__((address_space(3))) char lds_char;
+    for (int mb = 0; mb < MB; ++mb) {
+      vx[mb] = v_ring + (VL ^ (uint32_t)(mb << 6));
+      pin(vx[mb]);
+    }
     auto kfrag = [&](const lds_bf16 *kb, int half, int kc) KB_INLINE {
-      return *(const lds_bf16x8 *)((const lds_char *)kb + kx[kc] + half * 64 * D);
+      const uint32_t so = (uint32_t)((const lds_char *)kb - (const lds_char *)kst(0));
+      return *(const lds_bf16x8 *)((const lds_char *)(uintptr_t)kx[kc] + so + half * 64 * D);
     };
     // V^T fragment j of a tile: 32-row block mb = j % MB, 16-key chunk j / MB.
     auto vfrag = [&](const lds_bf16 *vb, int j) KB_INLINE {
       const int mb = j % MB, cc = j / MB;
-      const lds_char *a = (const lds_char *)vb + vx[mb] + cc * 32 * D;
+      const uint32_t so = (uint32_t)((const lds_char *)vb - (const lds_char *)vst(0));
+      const lds_char *a = (const lds_char *)(uintptr_t)vx[mb] + so + cc * 32 * D;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)a);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a + 16 * D));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
