@@ -18,7 +18,10 @@ The JSON line also carries:
                 seeded sample of the same workload's query rows (also used
                 to check the GPU output on those rows);
   triad         the HBM triad calibration (best of a block-size sweep);
-  variants      naive and fused on the same workload (a few timed calls).
+  variants      naive and fused on the same workload (a few timed calls);
+  per_config    flash on every configured workload (the metric is quoted per
+                (B, H, S, d), causal or not): mean hipEvent time per launch,
+                TFLOP/s and the fraction of the dtype's MFMA peak.
 """
 from __future__ import annotations
 
@@ -48,6 +51,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extras", action="store_true", help="skip triad and the naive/fused variants")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the flash table over every configured workload")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB three times "
                          "(a kernel of known traffic, used to scale the rocprofv3 byte counters)")
@@ -103,6 +108,30 @@ def cpu_baseline(p, o_gpu, budget_s, seed=1234):
                   f"{t_used:.1f} s; throughput scaled by the rows' algorithmic FLOPs",
         "max_abs_err_vs_gpu_on_sample": max(errs),
     }
+
+
+def per_config_table(kb, torch, inputs, stream, cache, iters=10):
+    """Flash on every configured workload (seeded inputs per the recipe; the
+    S=8192 workload also without the mask)."""
+    rows = []
+    for name in inputs.WORKLOADS:
+        p = cache[name] if name in cache else inputs.workload(name)
+        q, k, v = device_tensors(p, torch)
+        o = torch.empty((p.BH, p.S, p.d), dtype=torch.float32, device="cuda")
+        dt = kb.KB_BF16 if p.dtype == inputs.BF16 else kb.KB_F32
+        for causal in ([True, False] if name == "b2h32s8192d128_bf16_causal" else [p.causal]):
+            cfg = kb.make_cfg(p.B, p.H, p.S, p.d, causal, dt)
+            per, _ = kb.kb_bench_attention(cfg, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                           "flash", stream, 3, iters)
+            ms = float(np.mean(per))
+            fl = kb.attention_flops(p.B, p.H, p.S, p.d, causal)
+            tf = fl / (ms * 1e-3) / 1e12
+            rows.append({"workload": name, "B": p.B, "H": p.H, "S": p.S, "d": p.d, "causal": causal,
+                         "dtype": p.dtype, "kernel_ms_mean": round(ms, 4), "tflops": round(tf, 2),
+                         "frac_of_peak": round(tf / PEAK_TFLOPS[p.dtype], 4)})
+        del q, k, v, o
+        torch.cuda.empty_cache()
+    return rows
 
 
 def measured_traffic(workload):
@@ -230,6 +259,9 @@ def main():
         torch.cuda.empty_cache()
         result["variants"] = extras
         result["triad"] = triad_calibration(kb, torch, stream)
+
+    if not args.no_configs:
+        result["per_config"] = per_config_table(kb, torch, inputs, stream, {args.workload: p})
 
     if not args.no_cpu:
         kb.kb_attention(cfg, *ptrs, "flash", stream)
