@@ -24,46 +24,98 @@ namespace {
 constexpr int kThreads = 256;
 
 // ------------------------------------------------------------- pass 1 -----
-// Workgroup tile: 128 rows i x 128 columns j; wave w owns rows 32w..32w+31
-// and all four 32-column blocks.  Operands come straight from global memory
-// (both are contiguous along d, the contraction index); C = Q K^T with lane
-// (j % 32) holding one score column, so each store writes 128 contiguous
-// bytes per row.
-template <int D>
+// Workgroup tile: 128 keys j x 128 queries i, computed transposed,
+// W^T block = K Q^T: the K tile (128 x D) is staged once in LDS (rows padded
+// by 16 bytes) and read by all four waves; wave w keeps Q^T of its 32
+// queries i0 .. i0 + 31 in registers.  Lane (l32, h) then holds, for each
+// 32-key block jb, the scores of query i0 + l32 against keys
+// 32 jb + 8 r + 4 h + {0, 1, 2, 3}.  The scores leave through LDS (the K
+// tile's space, rows padded to 68 floats) in two halves of 64 keys, so each
+// store instruction writes four whole 256-byte pieces of rows; the pass is
+// bound by these HBM writes.
+template <int D, bool VEC>
 __global__ __launch_bounds__(kThreads) void scores_bf16_kernel(const bf16_t *__restrict__ Q,
                                                                const bf16_t *__restrict__ K,
                                                                float *__restrict__ W, int S,
                                                                float scale) {
+  constexpr int KC = D / 16;
+  constexpr int STR = D + 8;
+  constexpr int CPR = D / 8;
+  constexpr int NCH = 128 * CPR / kThreads;
+  // K tile (bf16, 128 x STR) or, after the MFMAs, four 32 x 68 fp32 blocks.
+  constexpr int LDS_BYTES = 128 * STR * 2 > 4 * 32 * 68 * 4 ? 128 * STR * 2 : 4 * 32 * 68 * 4;
+  __shared__ __attribute__((aligned(16))) float lds[LDS_BYTES / 4];
+  bf16_t *Ks = (bf16_t *)lds;
   const int bh = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int i0 = blockIdx.y * 128 + 32 * w;
   const int j0 = blockIdx.x * 128;
   const size_t base = (size_t)bh * S * D;
-  const bf16_t *qp = Q + base + (size_t)min(i0 + l32, S - 1) * D + 8 * h;
-  const bf16_t *kp[4];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) kp[jb] = K + base + (size_t)min(j0 + 32 * jb + l32, S - 1) * D + 8 * h;
+  for (int c = 0; c < NCH; ++c) {
+    const int idx = tid + c * kThreads;
+    const int row = idx / CPR, col = (idx % CPR) * 8;
+    const int key = j0 + row;
+    u32x4 val = u32x4{0, 0, 0, 0};
+    if (key < S) val = *(const u32x4 *)(K + base + (size_t)key * D + col);
+    *(u32x4 *)&Ks[row * STR + col] = val;
+  }
+  bf16x8 qf[KC];
+  const bf16_t *qp = Q + base + (size_t)min(i0 + l32, S - 1) * D + 8 * h;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) qf[kc] = *(const bf16x8 *)(qp + 16 * kc);
+  __syncthreads();
   f32x16 acc[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x16{};
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
-    const bf16x8 a = *(const bf16x8 *)(qp + 16 * kc);
+  for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) acc[jb] = mfma32x16_bf16(a, *(const bf16x8 *)(kp[jb] + 16 * kc), acc[jb]);
-  }
-  float *wp = W + (size_t)bh * S * S;
+    for (int jb = 0; jb < 4; ++jb)
+      acc[jb] = mfma32x16_bf16(*(const bf16x8 *)&Ks[(32 * jb + l32) * STR + 16 * kc + 8 * h], qf[kc], acc[jb]);
+  if (VEC) {
+    float *T = lds + w * 32 * 68;
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    const int j = j0 + 32 * jb + l32;
-    if (j >= S) continue;
+    for (int ph = 0; ph < 2; ++ph) {
+      __syncthreads();
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int i = i0 + acc_row(v, h);
-      if (i < S) wp[(size_t)i * S + j] = acc[jb][v] * scale;
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jb = 2 * ph + jj;
+          const f32x4 val = {acc[jb][4 * r] * scale, acc[jb][4 * r + 1] * scale, acc[jb][4 * r + 2] * scale,
+                             acc[jb][4 * r + 3] * scale};
+          *(f32x4 *)&T[l32 * 68 + 32 * jj + 8 * r + 4 * h] = val;
+        }
+      __syncthreads();
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int row = 4 * rr + (lane >> 4), col = 4 * (lane & 15);
+        const int i = i0 + row, j = j0 + 64 * ph + col;
+        const f32x4 val = *(const f32x4 *)&T[row * 68 + col];
+        if (i < S && j + 4 <= S) *(f32x4 *)(W + ((size_t)bh * S + i) * (size_t)S + j) = val;
+        else if (i < S)
+          for (int e = 0; e < 4; ++e)
+            if (j + e < S) W[((size_t)bh * S + i) * (size_t)S + j + e] = val[e];
+      }
     }
+    return;
   }
+  const int i = i0 + l32;
+  if (i >= S) return;
+  float *wp = W + ((size_t)bh * S + i) * (size_t)S + j0;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 32 * jb + 8 * r + 4 * h;
+      const f32x4 val = {acc[jb][4 * r] * scale, acc[jb][4 * r + 1] * scale, acc[jb][4 * r + 2] * scale,
+                         acc[jb][4 * r + 3] * scale};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + j + e < S) wp[j + e] = val[e];
+    }
 }
 
 // fp32: contraction step (g, e) uses d-column 8g + 4h + e from lane half h.
@@ -178,7 +230,10 @@ __global__ __launch_bounds__(kThreads) void softmax_any_kernel(float *__restrict
 // O^T = V^T P^T per workgroup of 128 query rows (wave w: rows 32w..32w+31);
 // 64-key V tiles staged in LDS and read transposed, P^T streamed from global
 // memory.  The key order inside each 16-key chunk matches the transposing
-// read: lane half h holds keys {4h..4h+3, 8+4h..8+4h+3}.
+// read: lane half h holds keys {4h..4h+3, 8+4h..8+4h+3}.  The global loads
+// of tile t+1 (its V rows and this lane's 32 probabilities) are issued before
+// tile t is computed, so their latency hides behind the MFMAs; the pass is
+// bound by the HBM reads of P.
 template <int D, bool VEC>
 __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float *__restrict__ W,
                                                            const bf16_t *__restrict__ V,
@@ -200,37 +255,60 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float *__restri
   f32x16 oacc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
+  // This thread's share of a V tile and this lane's probabilities of a tile
+  // (chunk c16: keys 16 c16 + 4h + {0..3} in slots 0-3, + 8 in slots 4-7).
+  u32x4 vreg[CH];
+  float pc[BC / 2], pn[BC / 2];
+  auto load_v = [&](int kt0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + c * kThreads;
+      const int row = idx / CPR, col = (idx % CPR) * 8;
+      const int key = kt0 + row;
+      vreg[c] = u32x4{0, 0, 0, 0};
+      if (key < S) vreg[c] = *(const u32x4 *)(V + base + (size_t)key * D + col);
+    }
+  };
+  auto load_p = [&](float *pv, int kt0) {
+#pragma unroll
+    for (int c16 = 0; c16 < BC / 16; ++c16) {
+      const int k0 = kt0 + 16 * c16 + 4 * h;
+      float *d = pv + 8 * c16;
+      if (VEC && k0 + 12 <= S) {
+        const float4 a = *(const float4 *)(prow + k0);
+        const float4 b = *(const float4 *)(prow + k0 + 8);
+        d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+        d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+      } else {
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+          const int key = k0 + (s8 < 4 ? s8 : 4 + s8);
+          d[s8] = key < S ? prow[key] : 0.f;
+        }
+      }
+    }
+  };
+  load_v(0);
+  load_p(pc, 0);
   for (int kt0 = 0; kt0 < S; kt0 += BC) {
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int idx = tid + c * kThreads;
       const int row = idx / CPR, col = (idx % CPR) * 8;
-      const int key = kt0 + row;
-      u32x4 val = u32x4{0, 0, 0, 0};
-      if (key < S) val = *(const u32x4 *)(V + base + (size_t)key * D + col);
-      *(u32x4 *)&Vs[row * STR + col] = val;
+      *(u32x4 *)&Vs[row * STR + col] = vreg[c];
     }
     __syncthreads();
+    const bool more = kt0 + BC < S;
+    if (more) {
+      load_v(kt0 + BC);
+      load_p(pn, kt0 + BC);
+    }
 #pragma unroll
     for (int c16 = 0; c16 < BC / 16; ++c16) {
-      const int k0 = kt0 + 16 * c16 + 4 * h;
-      float pv[8];
-      if (VEC && k0 + 12 <= S) {
-        const float4 a = *(const float4 *)(prow + k0);
-        const float4 b = *(const float4 *)(prow + k0 + 8);
-        pv[0] = a.x; pv[1] = a.y; pv[2] = a.z; pv[3] = a.w;
-        pv[4] = b.x; pv[5] = b.y; pv[6] = b.z; pv[7] = b.w;
-      } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int key = k0 + (s < 4 ? s : 4 + s);
-          pv[s] = key < S ? prow[key] : 0.f;
-        }
-      }
       bf16x8 pb;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) pb[s] = (bf16_t)pv[s];
+      for (int s8 = 0; s8 < 8; ++s8) pb[s8] = (bf16_t)pc[8 * c16 + s8];
       const bf16_t *vp = &Vs[(16 * c16 + tr_row) * STR + tr_col];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -241,6 +319,10 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float *__restri
         const auto a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[mb] = mfma32x16_bf16(__builtin_bit_cast(bf16x8, a), pb, oacc[mb]);
       }
+    }
+    if (more) {
+#pragma unroll
+      for (int e = 0; e < BC / 2; ++e) pc[e] = pn[e];
     }
   }
   if (q < S) {
@@ -321,8 +403,11 @@ template <int D>
 hipError_t launch_scores(const kb_problem &p) {
   const int nt = (p.S + 127) / 128;
   const dim3 grid(nt, nt, p.bh);
-  if (p.bf16)
-    hipLaunchKernelGGL((scores_bf16_kernel<D>), grid, dim3(kThreads), 0, p.stream,
+  if (p.bf16 && p.S % 4 == 0)
+    hipLaunchKernelGGL((scores_bf16_kernel<D, true>), grid, dim3(kThreads), 0, p.stream,
+                       (const bf16_t *)p.Q, (const bf16_t *)p.K, p.work, p.S, p.scale);
+  else if (p.bf16)
+    hipLaunchKernelGGL((scores_bf16_kernel<D, false>), grid, dim3(kThreads), 0, p.stream,
                        (const bf16_t *)p.Q, (const bf16_t *)p.K, p.work, p.S, p.scale);
   else
     hipLaunchKernelGGL((scores_f32_kernel<D>), grid, dim3(kThreads), 0, p.stream,
