@@ -124,6 +124,16 @@ def test_several_query_tiles_and_ragged_tail(variant):
             full_check(p, variant, f"B2H2S{S}/d{d}/{dtype}/{'c' if causal else 'nc'}/{variant}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_flash_work_split_over_xcds(causal):
+    """Slice counts that do not divide over the 8 XCDs (some get two slices,
+    some none) and odd query-tile counts (a causal unit with a single middle
+    tile), through the flash kernel's persistent schedule."""
+    for (B, H, S, d) in ((3, 3, 700, 128), (1, 17, 1300, 64), (1, 1, 2600, 128), (5, 2, 300, 32)):
+        p = inputs.make_problem(B, H, S, d, inputs.BF16, causal=causal, seed=B * 100 + H + S)
+        full_check(p, "flash", f"B{B}H{H}S{S}/d{d}/{'c' if causal else 'nc'}/flash")
+
+
 # ---------------------------------------------------------------- invariants through the GPU
 
 @pytest.mark.parametrize("variant", VARIANTS)
