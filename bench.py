@@ -21,7 +21,10 @@ The JSON line also carries:
   variants      naive and fused on the same workload (a few timed calls);
   per_config    flash on every configured workload (the metric is quoted per
                 (B, H, S, d), causal or not): mean hipEvent time per launch,
-                TFLOP/s and the fraction of the dtype's MFMA peak.
+                TFLOP/s and the fraction of the dtype's MFMA peak;
+  ceilings      sustained compute ceilings (kb_bench_ceiling: bf16 and fp32
+                MFMA, fp32 FMA, exp) with the shader clock the probe ran at,
+                the compute analogue of the triad.
 """
 from __future__ import annotations
 
@@ -53,6 +56,7 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip triad and the naive/fused variants")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the flash table over every configured workload")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the compute-ceiling probes")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB three times "
                          "(a kernel of known traffic, used to scale the rocprofv3 byte counters)")
@@ -132,6 +136,36 @@ def per_config_table(kb, torch, inputs, stream, cache, iters=10):
         del q, k, v, o
         torch.cuda.empty_cache()
     return rows
+
+
+# Datasheet peaks the ceilings are compared with (TFLOP/s; the fp32 vector
+# figure counts packed FMA, which the probe does not use, so its non-packed
+# bound is half of it) and the work per clock per CU of each probe.
+CEIL_PEAK = {"mfma_bf16": 2516.6, "mfma_f32": 157.3, "fma_f32": 157.3 / 2, "exp_f32": None}
+CEIL_PER_CLK_CU = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": None}
+
+
+def ceilings(kb, torch, stream, target_ms=40.0):
+    """Each probe sized to ~target_ms per launch, one warmup launch (so the
+    clock settles under load), then three timed ones."""
+    work = torch.empty(kb.kb_ceiling_work_size(), dtype=torch.uint8, device="cuda")
+    cus = kb.kb_device_info()["compute_units"]
+    out = {}
+    for kind in ("mfma_bf16", "mfma_f32", "fma_f32", "exp_f32"):
+        per, _, _ = kb.kb_bench_ceiling(kind, 2000, work.data_ptr(), work.numel(), stream, 1, 1)
+        iters = max(1, int(2000 * target_ms / max(per[0], 1e-3)))
+        per, ops, mhz = kb.kb_bench_ceiling(kind, iters, work.data_ptr(), work.numel(), stream, 1, 3)
+        ms = float(np.median(per))
+        rate = ops / (ms * 1e-3) / 1e12
+        row = {"unit": "Texp/s" if kind == "exp_f32" else "TFLOP/s", "value": round(rate, 2),
+               "clock_mhz": round(mhz, 0), "ms_per_launch": round(ms, 3), "iters": iters}
+        if CEIL_PEAK[kind]:
+            row["frac_of_datasheet_peak"] = round(rate / CEIL_PEAK[kind], 4)
+        if CEIL_PER_CLK_CU[kind] and mhz > 0:
+            row["peak_at_measured_clock"] = round(CEIL_PER_CLK_CU[kind] * cus * mhz * 1e6 / 1e12, 1)
+        out[kind] = row
+    del work
+    return out
 
 
 def measured_traffic(workload):
@@ -262,6 +296,9 @@ def main():
 
     if not args.no_configs:
         result["per_config"] = per_config_table(kb, torch, inputs, stream, {args.workload: p})
+
+    if not args.no_ceilings:
+        result["ceilings"] = ceilings(kb, torch, stream)
 
     if not args.no_cpu:
         kb.kb_attention(cfg, *ptrs, "flash", stream)

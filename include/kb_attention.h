@@ -127,6 +127,44 @@ kb_status kb_bench_triad(float *a, const float *b, const float *c, float s, size
                          int32_t block, void *stream, int32_t warmup, int32_t iters,
                          float *ms_per_iter, float *ms_total);
 
+/*
+ * Compute ceilings (the compute analogue of the triad; method of the
+ * micro-benchmark log page, section on compute peaks: independent
+ * instruction chains per thread, dense matrix products with fp32
+ * accumulation, the sustained clock recorded beside the result).  One
+ * workgroup per CU of eight waves, two per SIMD, each running `iters`
+ * iterations of 8 independent chains of one instruction:
+ */
+typedef enum {
+  KB_CEIL_MFMA_BF16 = 0, /* v_mfma_f32_32x32x16_bf16: 32768 flops each */
+  KB_CEIL_MFMA_F32 = 1,  /* v_mfma_f32_32x32x2f32: 4096 flops each */
+  KB_CEIL_FMA_F32 = 2,   /* v_fma_f32 (wave64): 128 flops each */
+  KB_CEIL_EXP_F32 = 3    /* v_exp_f32 (wave64): 64 exponentials each */
+} kb_ceiling_kind;
+
+/*
+ * Bytes of device work buffer kb_bench_ceiling needs on the current device
+ * (per-wave clock counters and one output float per thread); 0 if there is
+ * no device.
+ */
+size_t kb_ceiling_work_size(void);
+
+/*
+ * Timing helper for a ceiling probe, same protocol as kb_bench_attention:
+ * `warmup` untimed launches, then `reps` timed ones (ms_per_rep, host,
+ * length reps).  *ops_per_launch receives the operations one launch
+ * performs (flops for the MFMA and FMA kinds, exponentials for EXP).  If
+ * clock_mhz is non-NULL it receives the mean shader clock the waves of the
+ * last launch ran at (s_memtime over the 100 MHz s_memrealtime).  `work`:
+ * device buffer of >= kb_ceiling_work_size() bytes, owned by the caller
+ * (KB_ERR_WORKSPACE if smaller).  Errors: KB_ERR_INVALID for a bad kind,
+ * iters < 1, reps < 1, warmup < 0 or NULL result pointers; no device:
+ * KB_ERR_NO_DEVICE; not gfx950: KB_ERR_UNSUPPORTED.  Synchronises `stream`.
+ */
+kb_status kb_bench_ceiling(int32_t kind, int32_t iters, void *work, size_t work_bytes, void *stream,
+                           int32_t warmup, int32_t reps, float *ms_per_rep, double *ops_per_launch,
+                           float *clock_mhz);
+
 /* Properties of the current device, filled by kb_device_info. */
 typedef struct {
   char arch[64];              /* e.g. "gfx950:sramecc+:xnack-" */

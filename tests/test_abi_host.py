@@ -122,3 +122,30 @@ def test_flop_and_byte_counts():
     assert kb.attention_flops(2, 32, 8192, 128, True) == 1099645845504
     assert kb.attention_flops(1, 16, 32768, 128, False) == 8796093022208
     assert kb.attention_bytes(1, 1, 64, 32, 4) == 32 * 1024
+
+
+def test_ceiling_argument_checks():
+    import ctypes as ct
+    lib = kb.lib()
+    per = (ct.c_float * 2)()
+    ops = ct.c_double()
+    clk = ct.c_float()
+    # bad kind, iters, reps, warmup, NULL results: rejected before any device query
+    assert lib.kb_bench_ceiling(4, 10, FAKE, 1 << 20, None, 0, 2, per, ct.byref(ops), ct.byref(clk)) == 1
+    assert lib.kb_bench_ceiling(-1, 10, FAKE, 1 << 20, None, 0, 2, per, ct.byref(ops), ct.byref(clk)) == 1
+    assert lib.kb_bench_ceiling(0, 0, FAKE, 1 << 20, None, 0, 2, per, ct.byref(ops), ct.byref(clk)) == 1
+    assert lib.kb_bench_ceiling(0, 10, FAKE, 1 << 20, None, 0, 0, per, ct.byref(ops), ct.byref(clk)) == 1
+    assert lib.kb_bench_ceiling(0, 10, FAKE, 1 << 20, None, -1, 2, per, ct.byref(ops), ct.byref(clk)) == 1
+    assert lib.kb_bench_ceiling(0, 10, FAKE, 1 << 20, None, 0, 2, None, ct.byref(ops), ct.byref(clk)) == 1
+    assert lib.kb_bench_ceiling(0, 10, FAKE, 1 << 20, None, 0, 2, per, None, ct.byref(clk)) == 1
+
+
+def test_ceiling_without_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    import ctypes as ct
+    per = (ct.c_float * 2)()
+    ops = ct.c_double()
+    assert kb.kb_ceiling_work_size() == 0
+    assert kb.lib().kb_bench_ceiling(0, 10, FAKE, 1 << 20, None, 0, 2, per, ct.byref(ops), None) == 5

@@ -221,3 +221,20 @@ def test_device_info_is_gfx950():
     print(f"[device] {info}", flush=True)
     assert info["arch"].startswith("gfx950")
     assert info["compute_units"] > 0
+
+
+def test_compute_ceiling_probes_run():
+    """The ceiling probes run on the device and report sane rates and clocks."""
+    torch = torch_cuda()
+    work = torch.empty(kb.kb_ceiling_work_size(), dtype=torch.uint8, device="cuda")
+    cus = kb.kb_device_info()["compute_units"]
+    bound = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": 128}  # per clock per CU
+    for kind in kb.CEILINGS:
+        per, ops, mhz = kb.kb_bench_ceiling(kind, 200, work.data_ptr(), work.numel(), 0, 1, 2)
+        rate = ops / (min(per) * 1e-3)
+        print(f"[ceiling] {kind}: {rate / 1e12:.1f} T/s at {mhz:.0f} MHz", flush=True)
+        assert 300 < mhz < 3000
+        assert 0 < rate <= bound[kind] * cus * 3.0e9
+    with pytest.raises(kb.KbError) as ei:
+        kb.kb_bench_ceiling("mfma_bf16", 10, work.data_ptr(), 16, 0, 0, 1)
+    assert ei.value.status == 3

@@ -23,7 +23,9 @@ SIZE_MAX = 2 ** (8 * ctypes.sizeof(ctypes.c_size_t)) - 1
 
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = ("kb_attention", "kb_attention_workspace_size", "kb_triad", "kb_bench_attention",
-           "kb_bench_triad", "kb_device_info", "kb_status_string", "kb_last_error")
+           "kb_bench_triad", "kb_ceiling_work_size", "kb_bench_ceiling", "kb_device_info",
+           "kb_status_string", "kb_last_error")
+CEILINGS = {"mfma_bf16": 0, "mfma_f32": 1, "fma_f32": 2, "exp_f32": 3}
 
 
 class KbAttnCfg(ctypes.Structure):
@@ -68,6 +70,10 @@ def lib() -> ctypes.CDLL:
         h.kb_bench_attention.restype = i32
         h.kb_bench_triad.argtypes = [vp, vp, vp, f32, sz, i32, vp, i32, i32, fp, fp]
         h.kb_bench_triad.restype = i32
+        h.kb_ceiling_work_size.argtypes = []
+        h.kb_ceiling_work_size.restype = sz
+        h.kb_bench_ceiling.argtypes = [i32, i32, vp, sz, vp, i32, i32, fp, ctypes.POINTER(ctypes.c_double), fp]
+        h.kb_bench_ceiling.restype = i32
         h.kb_device_info.argtypes = [ctypes.POINTER(KbDeviceProps)]
         h.kb_device_info.restype = i32
         h.kb_status_string.argtypes = [i32]
@@ -127,6 +133,21 @@ def kb_bench_triad(a: int, b: int, c: int, s: float, n: int, block: int, stream:
     _check(lib().kb_bench_triad(a, b, c, s, n, block, stream or None, warmup, iters, per,
                                 ctypes.byref(tot)), "kb_bench_triad")
     return list(per), tot.value
+
+
+def kb_ceiling_work_size() -> int:
+    return lib().kb_ceiling_work_size()
+
+
+def kb_bench_ceiling(kind, iters: int, work: int, work_bytes: int, stream: int, warmup: int, reps: int):
+    """Returns (ms per timed launch, operations per launch, mean shader clock in MHz)."""
+    per = (ctypes.c_float * reps)()
+    ops = ctypes.c_double()
+    clk = ctypes.c_float()
+    k = CEILINGS[kind] if isinstance(kind, str) else int(kind)
+    _check(lib().kb_bench_ceiling(k, iters, work or None, work_bytes, stream or None, warmup, reps, per,
+                                  ctypes.byref(ops), ctypes.byref(clk)), "kb_bench_ceiling")
+    return list(per), ops.value, clk.value
 
 
 def kb_device_info() -> dict:

@@ -319,6 +319,65 @@ kb_status kb_bench_triad(float *a, const float *b, const float *c, float s, size
       hs, warmup, iters, ms_per_iter, ms_total);
 }
 
+size_t kb_ceiling_work_size(void) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 0;
+  return (size_t)kb_ceiling_waves(cus) * 2 * sizeof(unsigned long long) + (size_t)cus * 512 * sizeof(float);
+}
+
+kb_status kb_bench_ceiling(int32_t kind, int32_t iters, void *work, size_t work_bytes, void *stream,
+                           int32_t warmup, int32_t reps, float *ms_per_rep, double *ops_per_launch,
+                           float *clock_mhz) {
+  if (kind < KB_CEIL_MFMA_BF16 || kind > KB_CEIL_EXP_F32) {
+    set_err("kind %d is not a kb_ceiling_kind", kind);
+    return KB_ERR_INVALID;
+  }
+  if (iters < 1 || reps < 1 || warmup < 0 || !ms_per_rep || !ops_per_launch) {
+    set_err("iters >= 1, reps >= 1, warmup >= 0 and non-NULL results are required");
+    return KB_ERR_INVALID;
+  }
+  kb_status st = device_check(nullptr);
+  if (st != KB_OK) return st;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "multiprocessor count");
+  const size_t waves = (size_t)kb_ceiling_waves(cus);
+  const size_t need = waves * 2 * sizeof(unsigned long long) + (size_t)cus * 512 * sizeof(float);
+  if (!work || work_bytes < need) {
+    set_err("work buffer of %zu bytes needed (got %zu)", need, work ? work_bytes : (size_t)0);
+    return KB_ERR_WORKSPACE;
+  }
+  unsigned long long *clk = (unsigned long long *)work;
+  float *sink = (float *)(clk + 2 * waves);
+  hipStream_t hs = (hipStream_t)stream;
+  float total = 0.f;
+  st = bench_loop(
+      [&]() {
+        hipError_t le = kb_launch_ceiling(kind, cus, iters, clk, sink, hs);
+        return le == hipSuccess ? KB_OK : hip_fail(le, "ceiling launch");
+      },
+      hs, warmup, reps, ms_per_rep, &total);
+  if (st != KB_OK) return st;
+  *ops_per_launch = kb_ceiling_ops(kind, cus, iters);
+  if (clock_mhz) {
+    std::vector<unsigned long long> h(2 * waves);
+    e = hipMemcpy(h.data(), clk, h.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "reading the clock counters");
+    double sum = 0.0;
+    size_t n = 0;
+    for (size_t w = 0; w < waves; ++w)
+      if (h[2 * w + 1] > 0) {
+        sum += (double)h[2 * w] / ((double)h[2 * w + 1] / 100.0);
+        ++n;
+      }
+    *clock_mhz = n ? (float)(sum / (double)n) : 0.f;
+  }
+  return KB_OK;
+}
+
 kb_status kb_device_info(kb_device_props *out) {
   if (!out) {
     set_err("out is NULL");

@@ -124,3 +124,10 @@ hipError_t kb_launch_fused(const kb_problem &p);
 size_t kb_fused_lds_bytes(const kb_problem &p);
 hipError_t kb_launch_triad(float *a, const float *b, const float *c, float s, size_t n, int block,
                            hipStream_t stream);
+// Compute-ceiling probes (ceiling.hip): waves one launch runs on `cus` CUs,
+// operations it performs, and the launch itself (clk: 2 counters per wave,
+// sink: one float per thread).
+int kb_ceiling_waves(int cus);
+double kb_ceiling_ops(int kind, int cus, int iters);
+hipError_t kb_launch_ceiling(int kind, int cus, int iters, unsigned long long *clk, float *sink,
+                             hipStream_t stream);
