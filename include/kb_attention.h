@@ -64,11 +64,12 @@ typedef enum {
 
 /*
  * One attention problem.  Q, K, V are [batch*heads, seq, dim] row-major of
- * type in_dtype; O is [batch*heads, seq, dim] row-major fp32.
+ * type in_dtype; O is [batch*heads, seq, dim] row-major of type out_dtype.
  *   batch, heads >= 1, seq >= 1 (any length: tails are masked),
  *   dim in {32, 64, 128},
  *   causal 0 or 1,
- *   in_dtype KB_F32 or KB_BF16, out_dtype KB_F32 (the only output type),
+ *   in_dtype KB_F32 or KB_BF16, out_dtype KB_F32 or KB_BF16 (bf16 output is the
+ *   fp32 result rounded to nearest even, in the kernels' epilogue),
  *   scale: the logit scale; 0.0f means 1/sqrt(dim).  It is applied in fp32
  *          to the fp32 dot products, never folded into the inputs.
  *   workspace / workspace_bytes: device scratch, used by KB_NAIVE only
@@ -81,7 +82,7 @@ typedef struct {
   int32_t batch, heads, seq, dim;
   int32_t causal;
   int32_t in_dtype;  /* kb_dtype */
-  int32_t out_dtype; /* kb_dtype, KB_F32 */
+  int32_t out_dtype; /* kb_dtype of O */
   float scale;
   void *workspace;
   size_t workspace_bytes;

@@ -82,8 +82,8 @@ def test_unsupported_dims_and_sizes():
     assert status_of(cfg(dim=256)) == 2
     assert status_of(cfg(batch=1, heads=1, seq=1 << 24, dim=128)) == 2
     c = cfg()
-    c.out_dtype = kb.KB_BF16
-    assert status_of(c) == 2
+    c.out_dtype = 5
+    assert status_of(c) == 1
 
 
 def test_misaligned_or_overlapping_buffers():
@@ -105,6 +105,9 @@ def test_valid_call_without_device_reports_no_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert status_of(cfg()) == 5
+    c = cfg()
+    c.out_dtype = kb.KB_BF16
+    assert status_of(c) == 5
     assert "device" in kb.lib().kb_last_error().decode().lower() or kb.lib().kb_last_error()
 
 

@@ -13,7 +13,7 @@ import pytest
 import oracle
 import transformer_attention_micro_amd as kb
 from transformer_attention_micro_amd import inputs
-from tests.gpu_util import (compare, nan_output, oracle_full, oracle_rows, sample_rows, to_device,
+from tests.gpu_util import (TOL, compare, nan_output, oracle_full, oracle_rows, sample_rows, to_device,
                             torch_cuda)
 
 pytestmark = pytest.mark.gpu
@@ -132,6 +132,31 @@ def test_flash_work_split_over_xcds(causal):
     for (B, H, S, d) in ((3, 3, 700, 128), (1, 17, 1300, 64), (1, 1, 2600, 128), (5, 2, 300, 32)):
         p = inputs.make_problem(B, H, S, d, inputs.BF16, causal=causal, seed=B * 100 + H + S)
         full_check(p, "flash", f"B{B}H{H}S{S}/d{d}/{'c' if causal else 'nc'}/flash")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bf16_output(variant):
+    """out_dtype bf16 is the fp32 result rounded to nearest even: bit-exact
+    against rounding the fp32 output of the same call on the host, hence
+    within the fp32 tolerance plus one bf16 ulp of the oracle."""
+    torch = torch_cuda()
+    for dtype, d, S, causal in ((inputs.BF16, 128, 700, True), (inputs.F32, 64, 333, False),
+                                (inputs.BF16, 32, 129, False)):
+        p = inputs.make_problem(2, 3, S, d, dtype, causal=causal, seed=S + d)
+        q, k, v = to_device(p)
+        o32 = kb.attention(q, k, v, causal=causal, variant=variant, heads=p.H)
+        ob = torch.full(o32.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        kb.attention(q, k, v, ob, causal=causal, variant=variant, heads=p.H)
+        torch.cuda.synchronize()
+        want_bits = inputs.bf16_bits(o32.cpu().numpy())
+        got_bits = ob.cpu().view(torch.int16).numpy().view(np.uint16)
+        label = f"bf16-out/S{S}/d{d}/{dtype}/{variant}"
+        assert np.array_equal(got_bits, want_bits), label
+        got = inputs.bf16_bits_to_f32(got_bits).astype(np.float64)
+        ref = oracle_full(p)
+        _, e = np.frexp(np.abs(ref))
+        ulp = np.ldexp(1.0, e - 8)
+        assert np.all(np.abs(got - ref) <= TOL[dtype] + ulp), label
 
 
 # ---------------------------------------------------------------- invariants through the GPU

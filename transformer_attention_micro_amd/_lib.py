@@ -90,8 +90,9 @@ def _check(status: int, where: str) -> None:
 
 
 def make_cfg(batch: int, heads: int, seq: int, dim: int, causal: bool, dtype: int,
-             scale: float = 0.0, workspace: int = 0, workspace_bytes: int = 0) -> KbAttnCfg:
-    return KbAttnCfg(batch, heads, seq, dim, int(bool(causal)), dtype, KB_F32, float(scale),
+             scale: float = 0.0, workspace: int = 0, workspace_bytes: int = 0,
+             out_dtype: int = KB_F32) -> KbAttnCfg:
+    return KbAttnCfg(batch, heads, seq, dim, int(bool(causal)), dtype, out_dtype, float(scale),
                      workspace or None, workspace_bytes)
 
 
@@ -196,10 +197,11 @@ def attention(q, k, v, out=None, *, causal: bool = False, variant="flash", scale
     """O = softmax(scale * Q K^T [causal]) V through kb_attention.
 
     q, k, v: contiguous CUDA tensors of one shape, [B, H, S, d] or [B*H, S, d],
-    float32 or bfloat16.  out: optional float32 tensor of the same shape.
-    variant "naive" needs a uint8/float CUDA workspace of at least
-    workspace_size(...) bytes; one is allocated (outside the kernels) when not
-    given.  Returns the fp32 output tensor.
+    float32 or bfloat16.  out: optional float32 or bfloat16 tensor of the same
+    shape (bfloat16: the fp32 result rounded to nearest even); a float32 one
+    is allocated when not given.  variant "naive" needs a uint8/float CUDA
+    workspace of at least workspace_size(...) bytes; one is allocated (outside
+    the kernels) when not given.  Returns the output tensor.
     """
     import torch
     for t in (q, k, v):
@@ -210,9 +212,10 @@ def attention(q, k, v, out=None, *, causal: bool = False, variant="flash", scale
     B, H, S, d = _shape(q, heads)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    elif out.dtype != torch.float32 or out.shape != q.shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 tensor shaped like Q")
-    cfg = make_cfg(B, H, S, d, causal, _dtype_code(q), scale)
+    elif out.dtype not in (torch.float32, torch.bfloat16) or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 or bfloat16 tensor shaped like Q")
+    cfg = make_cfg(B, H, S, d, causal, _dtype_code(q), scale,
+                   out_dtype=KB_BF16 if out.dtype == torch.bfloat16 else KB_F32)
     vcode = _variant(variant)
     if vcode == KB_NAIVE:
         need = kb_attention_workspace_size(cfg, vcode)

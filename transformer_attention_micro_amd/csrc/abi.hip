@@ -101,10 +101,6 @@ kb_status validate(const kb_attn_cfg *cfg, int32_t variant, kb_problem *p) {
     set_err("scale must be finite and >= 0 (0 selects 1/sqrt(dim))");
     return KB_ERR_INVALID;
   }
-  if (cfg->out_dtype != KB_F32) {
-    set_err("only fp32 output is implemented");
-    return KB_ERR_UNSUPPORTED;
-  }
   if (cfg->dim != 32 && cfg->dim != 64 && cfg->dim != 128) {
     set_err("dim %d unsupported (32, 64 or 128)", cfg->dim);
     return KB_ERR_UNSUPPORTED;
@@ -124,6 +120,7 @@ kb_status validate(const kb_attn_cfg *cfg, int32_t variant, kb_problem *p) {
   p->D = cfg->dim;
   p->causal = cfg->causal;
   p->bf16 = cfg->in_dtype == KB_BF16;
+  p->out_bf16 = cfg->out_dtype == KB_BF16;
   p->scale = cfg->scale > 0.f ? cfg->scale : (float)(1.0 / std::sqrt((double)cfg->dim));
   return KB_OK;
 }
@@ -140,7 +137,7 @@ kb_status prepare(const kb_attn_cfg *cfg, const void *Q, const void *K, const vo
   }
   const size_t esz = p->bf16 ? 2 : 4;
   const size_t in_bytes = (size_t)p->bh * p->S * p->D * esz;
-  const size_t out_bytes = (size_t)p->bh * p->S * p->D * 4;
+  const size_t out_bytes = (size_t)p->bh * p->S * p->D * (p->out_bf16 ? 2 : 4);
   auto overlap = [](const void *a, size_t na, const void *b, size_t nb) {
     const char *x = (const char *)a, *y = (const char *)b;
     return x < y + nb && y < x + na;
@@ -157,7 +154,7 @@ kb_status prepare(const kb_attn_cfg *cfg, const void *Q, const void *K, const vo
   p->Q = Q;
   p->K = K;
   p->V = V;
-  p->O = (float *)O;
+  p->O = O;
   p->work = nullptr;
   p->stream = (hipStream_t)stream;
   if (variant == KB_NAIVE) {

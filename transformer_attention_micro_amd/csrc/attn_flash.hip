@@ -161,7 +161,7 @@ constexpr int kPre = 4;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bf16_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
-    float *__restrict__ O, int S, int nbh, int nqt, float sl2e) {
+    void *__restrict__ O, int out_bf16, int S, int nbh, int nqt, float sl2e) {
   constexpr int BC = 64;                 // keys per tile
   constexpr int KC = D / 16;             // bf16 MFMA steps along d for S^T
   constexpr int MB = D / 32;             // 32-row blocks of O^T
@@ -635,14 +635,14 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
 
     const float inv = 1.f / xor32_sum(l_run);
     if (q < S) {
-      float *op = O + base + (size_t)q * D + 4 * h;
+      const size_t op = base + (size_t)q * D + 4 * h;
   #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
   #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const f32x4 o4 = {oacc[mb][4 * r] * inv, oacc[mb][4 * r + 1] * inv,
                             oacc[mb][4 * r + 2] * inv, oacc[mb][4 * r + 3] * inv};
-          *(f32x4 *)(op + 32 * mb + 8 * r) = o4;
+          store_out4(O, op + 32 * mb + 8 * r, o4, out_bf16);
         }
     }
   };
@@ -666,7 +666,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void flash_f32_kernel(const float *__restrict__ Q,
                                                              const float *__restrict__ K,
                                                              const float *__restrict__ V,
-                                                             float *__restrict__ O, int S, int nbh,
+                                                             void *__restrict__ O, int out_bf16, int S, int nbh,
                                                              int nqt, float sl2e) {
   constexpr int BC = 32;
   constexpr int STR = D + 4;  // 16-byte aligned rows, 4-bank shift per row
@@ -786,14 +786,14 @@ __global__ __launch_bounds__(kThreads) void flash_f32_kernel(const float *__rest
 
   const float inv = 1.f / xor32_sum(l_run);
   if (q < S) {
-    float *op = O + base + (size_t)q * D + 4 * h;
+    const size_t op = base + (size_t)q * D + 4 * h;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const f32x4 o4 = {oacc[mb][4 * r] * inv, oacc[mb][4 * r + 1] * inv,
                           oacc[mb][4 * r + 2] * inv, oacc[mb][4 * r + 3] * inv};
-        *(f32x4 *)(op + 32 * mb + 8 * r) = o4;
+        store_out4(O, op + 32 * mb + 8 * r, o4, out_bf16);
       }
   }
 }
@@ -830,11 +830,11 @@ hipError_t launch_d(const kb_problem &p) {
   const float sl2e = p.scale * kLog2e;
   if (p.bf16)
     hipLaunchKernelGGL((flash_bf16_kernel<D, CAUSAL>), grid_b, dim3(kThreadsB), 0, p.stream,
-                       (const bf16_t *)p.Q, (const bf16_t *)p.K, (const bf16_t *)p.V, p.O, p.S, p.bh,
+                       (const bf16_t *)p.Q, (const bf16_t *)p.K, (const bf16_t *)p.V, p.O, p.out_bf16, p.S, p.bh,
                        nqt, sl2e);
   else
     hipLaunchKernelGGL((flash_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, p.stream,
-                       (const float *)p.Q, (const float *)p.K, (const float *)p.V, p.O, p.S, p.bh,
+                       (const float *)p.Q, (const float *)p.K, (const float *)p.V, p.O, p.out_bf16, p.S, p.bh,
                        nqt, sl2e);
   return hipGetLastError();
 }

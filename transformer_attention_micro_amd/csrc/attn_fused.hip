@@ -49,8 +49,8 @@ struct Elem<float> {
 
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ Q, const T *__restrict__ K,
-                                                         const T *__restrict__ V, float *__restrict__ O,
-                                                         int S, int causal, float scale) {
+                                                         const T *__restrict__ V, void *__restrict__ O,
+                                                         int out_bf16, int S, int causal, float scale) {
   constexpr int EPC = Elem<T>::kPerChunk;
   constexpr int CPR = D / EPC;            // 16-byte chunks per row = lanes per key
   constexpr int KPW = kWave / CPR;        // keys per wave step
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ Q
   if (tid < D) {
     float o = 0.f;
     for (int g = 0; g < G; ++g) o += part[g * D + tid];
-    O[base + (size_t)i * D + tid] = o / l;
+    store_out1(O, base + (size_t)i * D + tid, o / l, out_bf16);
   }
 }
 
@@ -140,7 +140,7 @@ hipError_t launch_t(const kb_problem &p) {
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((size_t)p.bh * p.S));
   hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, p.stream, (const T *)p.Q, (const T *)p.K,
-                     (const T *)p.V, p.O, p.S, p.causal, p.scale);
+                     (const T *)p.V, p.O, p.out_bf16, p.S, p.causal, p.scale);
   return hipGetLastError();
 }
 

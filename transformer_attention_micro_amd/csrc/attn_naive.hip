@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void softmax_any_kernel(float *__restrict
 template <int D, bool VEC>
 __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float *__restrict__ W,
                                                            const bf16_t *__restrict__ V,
-                                                           float *__restrict__ O, int S) {
+                                                           void *__restrict__ O, int out_bf16, int S) {
   constexpr int BC = 64;
   constexpr int STR = D + 8;
   constexpr int MB = D / 32;
@@ -326,13 +326,14 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float *__restri
     }
   }
   if (q < S) {
-    float *op = O + base + (size_t)q * D + 4 * h;
+    const size_t op = base + (size_t)q * D + 4 * h;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        *(f32x4 *)(op + 32 * mb + 8 * r) =
-            f32x4{oacc[mb][4 * r], oacc[mb][4 * r + 1], oacc[mb][4 * r + 2], oacc[mb][4 * r + 3]};
+        store_out4(O, op + 32 * mb + 8 * r,
+                   f32x4{oacc[mb][4 * r], oacc[mb][4 * r + 1], oacc[mb][4 * r + 2], oacc[mb][4 * r + 3]},
+                   out_bf16);
   }
 }
 
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float *__restri
 template <int D, bool VEC>
 __global__ __launch_bounds__(kThreads) void pv_f32_kernel(const float *__restrict__ W,
                                                           const float *__restrict__ V,
-                                                          float *__restrict__ O, int S) {
+                                                          void *__restrict__ O, int out_bf16, int S) {
   constexpr int BC = 32;
   constexpr int STR = D + 4;
   constexpr int MB = D / 32;
@@ -389,13 +390,14 @@ __global__ __launch_bounds__(kThreads) void pv_f32_kernel(const float *__restric
     }
   }
   if (q < S) {
-    float *op = O + base + (size_t)q * D + 4 * h;
+    const size_t op = base + (size_t)q * D + 4 * h;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        *(f32x4 *)(op + 32 * mb + 8 * r) =
-            f32x4{oacc[mb][4 * r], oacc[mb][4 * r + 1], oacc[mb][4 * r + 2], oacc[mb][4 * r + 3]};
+        store_out4(O, op + 32 * mb + 8 * r,
+                   f32x4{oacc[mb][4 * r], oacc[mb][4 * r + 1], oacc[mb][4 * r + 2], oacc[mb][4 * r + 3]},
+                   out_bf16);
   }
 }
 
@@ -439,17 +441,17 @@ hipError_t launch_pv(const kb_problem &p) {
   if (p.bf16) {
     if (vec)
       hipLaunchKernelGGL((pv_bf16_kernel<D, true>), grid, dim3(kThreads), 0, p.stream, p.work,
-                         (const bf16_t *)p.V, p.O, p.S);
+                         (const bf16_t *)p.V, p.O, p.out_bf16, p.S);
     else
       hipLaunchKernelGGL((pv_bf16_kernel<D, false>), grid, dim3(kThreads), 0, p.stream, p.work,
-                         (const bf16_t *)p.V, p.O, p.S);
+                         (const bf16_t *)p.V, p.O, p.out_bf16, p.S);
   } else {
     if (vec)
       hipLaunchKernelGGL((pv_f32_kernel<D, true>), grid, dim3(kThreads), 0, p.stream, p.work,
-                         (const float *)p.V, p.O, p.S);
+                         (const float *)p.V, p.O, p.out_bf16, p.S);
     else
       hipLaunchKernelGGL((pv_f32_kernel<D, false>), grid, dim3(kThreads), 0, p.stream, p.work,
-                         (const float *)p.V, p.O, p.S);
+                         (const float *)p.V, p.O, p.out_bf16, p.S);
   }
   return hipGetLastError();
 }

@@ -98,6 +98,21 @@ __device__ __forceinline__ float block_sum(float x, float *red) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Four consecutive outputs at element `idx` of O (idx a multiple of 4): fp32,
+// or rounded to bf16 (round to nearest even) when out_bf16.
+__device__ __forceinline__ void store_out4(void *O, size_t idx, f32x4 v, int out_bf16) {
+  if (out_bf16)
+    *(bf16x4 *)((bf16_t *)O + idx) = bf16x4{(bf16_t)v[0], (bf16_t)v[1], (bf16_t)v[2], (bf16_t)v[3]};
+  else
+    *(f32x4 *)((float *)O + idx) = v;
+}
+__device__ __forceinline__ void store_out1(void *O, size_t idx, float v, int out_bf16) {
+  if (out_bf16)
+    ((bf16_t *)O)[idx] = (bf16_t)v;
+  else
+    ((float *)O)[idx] = v;
+}
+
 // bf16 pattern -> fp32 value (exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -112,7 +127,8 @@ struct kb_problem {
   int bf16;  // 1: Q/K/V are bf16 patterns, 0: fp32
   float scale;
   const void *Q, *K, *V;
-  float *O;
+  void *O;      // fp32, or bf16 patterns when out_bf16
+  int out_bf16;
   float *work;  // naive only
   hipStream_t stream;
 };
