@@ -18,6 +18,8 @@ The JSON line also carries:
                 seeded sample of the same workload's query rows (also used
                 to check the GPU output on those rows);
   triad         the HBM triad calibration (best of a block-size sweep);
+  hbm_reference copy, read-only and write-only kernels at the same 2 GiB
+                working set (best of the same sweep);
   variants      naive and fused on the same workload (a few timed calls);
   per_config    flash on every configured workload (the metric is quoted per
                 (B, H, S, d), causal or not): mean hipEvent time per launch,
@@ -293,6 +295,12 @@ def main():
         torch.cuda.empty_cache()
         result["variants"] = extras
         result["triad"] = triad_calibration(kb, torch, stream)
+        from transformer_attention_micro_amd.hbm import best_gbs
+        ref = {}
+        for kind in ("copy", "read", "write"):
+            gbs, block = best_gbs(kb, torch, kind, 2048, (64, 128, 256, 512, 1024), stream, 10, 30)
+            ref[kind] = {"gbs": round(gbs, 1), "block": block, "frac_of_8000": round(gbs / HBM_PEAK_GBS, 4)}
+        result["hbm_reference"] = ref
 
     if not args.no_configs:
         result["per_config"] = per_config_table(kb, torch, inputs, stream, {args.workload: p})

@@ -129,6 +129,23 @@ kb_status kb_bench_triad(float *a, const float *b, const float *c, float s, size
                          float *ms_per_iter, float *ms_total);
 
 /*
+ * The reference bandwidth kernels beside the triad (same page, "HBM
+ * Bandwidth"), timed with the same protocol, 128-bit accesses:
+ *   KB_STREAM_COPY   a[i] = b[i]           8 bytes per element
+ *   KB_STREAM_READ   read b[i], no writes  4 bytes per element
+ *   KB_STREAM_WRITE  a[i] = s              4 bytes per element
+ * n: elements, a multiple of 4, >= 4; a and b: 16-byte aligned,
+ * non-overlapping fp32 device buffers of n elements (b is not read by WRITE;
+ * READ stores a thread's sum into a only if it equals s, so pass s = NaN to
+ * write nothing).  block as for kb_triad.  KB_ERR_INVALID for a bad kind, n
+ * or block, or NULL, misaligned or overlapping buffers.
+ */
+typedef enum { KB_STREAM_COPY = 1, KB_STREAM_READ = 2, KB_STREAM_WRITE = 3 } kb_stream_kind;
+kb_status kb_bench_stream(int32_t kind, float *a, const float *b, float s, size_t n, int32_t block,
+                          void *stream, int32_t warmup, int32_t iters, float *ms_per_iter,
+                          float *ms_total);
+
+/*
  * Compute ceilings (the compute analogue of the triad; method of the
  * micro-benchmark log page, section on compute peaks: independent
  * instruction chains per thread, dense matrix products with fp32

@@ -152,3 +152,19 @@ def test_ceiling_without_device():
     ops = ct.c_double()
     assert kb.kb_ceiling_work_size() == 0
     assert kb.lib().kb_bench_ceiling(0, 10, FAKE, 1 << 20, None, 0, 2, per, ct.byref(ops), None) == 5
+
+
+def test_stream_argument_checks():
+    import ctypes as ct
+    lib = kb.lib()
+    per = (ct.c_float * 2)()
+    tot = ct.c_float()
+    ok = (FAKE, FAKE * 2)
+    assert lib.kb_bench_stream(0, *ok, 1.0, 1024, 256, None, 0, 2, per, ct.byref(tot)) == 1   # kind
+    assert lib.kb_bench_stream(4, *ok, 1.0, 1024, 256, None, 0, 2, per, ct.byref(tot)) == 1
+    assert lib.kb_bench_stream(1, *ok, 1.0, 1022, 256, None, 0, 2, per, ct.byref(tot)) == 1   # n % 4
+    assert lib.kb_bench_stream(1, *ok, 1.0, 0, 256, None, 0, 2, per, ct.byref(tot)) == 1
+    assert lib.kb_bench_stream(1, FAKE + 4, FAKE * 2, 1.0, 1024, 256, None, 0, 2, per, ct.byref(tot)) == 1
+    assert lib.kb_bench_stream(1, FAKE, FAKE + 64, 1.0, 1024, 256, None, 0, 2, per, ct.byref(tot)) == 1
+    assert lib.kb_bench_stream(1, *ok, 1.0, 1024, 100, None, 0, 2, per, ct.byref(tot)) == 1   # block
+    assert lib.kb_bench_stream(1, None, FAKE, 1.0, 1024, 256, None, 0, 2, per, ct.byref(tot)) == 1

@@ -263,3 +263,23 @@ def test_compute_ceiling_probes_run():
     with pytest.raises(kb.KbError) as ei:
         kb.kb_bench_ceiling("mfma_bf16", 10, work.data_ptr(), 16, 0, 0, 1)
     assert ei.value.status == 3
+
+
+def test_bandwidth_kernels_move_the_right_bytes():
+    """copy writes b into a, write fills a with s, read (with s = NaN) leaves a
+    untouched; the triad matches b + s c."""
+    torch = torch_cuda()
+    n = (1 << 20) + 12
+    b = torch.rand(n, device="cuda")
+    c = torch.rand(n, device="cuda")
+    for kind in ("copy", "read", "write"):
+        a = torch.full((n,), -7.0, device="cuda")
+        s = float("nan") if kind == "read" else 2.5
+        kb.kb_bench_stream(kind, a.data_ptr(), b.data_ptr(), s, n, 256, 0, 1, 2)
+        torch.cuda.synchronize()
+        want = {"copy": b, "read": torch.full_like(a, -7.0), "write": torch.full_like(a, 2.5)}[kind]
+        assert torch.equal(a, want), kind
+    a = torch.empty(n, device="cuda")
+    kb.triad(a, b, c, 1.5)
+    torch.cuda.synchronize()
+    assert torch.allclose(a, b + 1.5 * c, rtol=0, atol=1e-6)

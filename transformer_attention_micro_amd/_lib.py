@@ -23,9 +23,11 @@ SIZE_MAX = 2 ** (8 * ctypes.sizeof(ctypes.c_size_t)) - 1
 
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = ("kb_attention", "kb_attention_workspace_size", "kb_triad", "kb_bench_attention",
-           "kb_bench_triad", "kb_ceiling_work_size", "kb_bench_ceiling", "kb_device_info",
+           "kb_bench_triad", "kb_bench_stream", "kb_ceiling_work_size", "kb_bench_ceiling", "kb_device_info",
            "kb_status_string", "kb_last_error")
 CEILINGS = {"mfma_bf16": 0, "mfma_f32": 1, "fma_f32": 2, "exp_f32": 3}
+STREAMS = {"copy": 1, "read": 2, "write": 3}
+STREAM_BYTES = {"triad": 12, "copy": 8, "read": 4, "write": 4}  # per fp32 element
 
 
 class KbAttnCfg(ctypes.Structure):
@@ -70,6 +72,8 @@ def lib() -> ctypes.CDLL:
         h.kb_bench_attention.restype = i32
         h.kb_bench_triad.argtypes = [vp, vp, vp, f32, sz, i32, vp, i32, i32, fp, fp]
         h.kb_bench_triad.restype = i32
+        h.kb_bench_stream.argtypes = [i32, vp, vp, f32, sz, i32, vp, i32, i32, fp, fp]
+        h.kb_bench_stream.restype = i32
         h.kb_ceiling_work_size.argtypes = []
         h.kb_ceiling_work_size.restype = sz
         h.kb_bench_ceiling.argtypes = [i32, i32, vp, sz, vp, i32, i32, fp, ctypes.POINTER(ctypes.c_double), fp]
@@ -133,6 +137,16 @@ def kb_bench_triad(a: int, b: int, c: int, s: float, n: int, block: int, stream:
     tot = ctypes.c_float()
     _check(lib().kb_bench_triad(a, b, c, s, n, block, stream or None, warmup, iters, per,
                                 ctypes.byref(tot)), "kb_bench_triad")
+    return list(per), tot.value
+
+
+def kb_bench_stream(kind, a: int, b: int, s: float, n: int, block: int, stream: int, warmup: int,
+                    iters: int):
+    per = (ctypes.c_float * iters)()
+    tot = ctypes.c_float()
+    k = STREAMS[kind] if isinstance(kind, str) else int(kind)
+    _check(lib().kb_bench_stream(k, a, b, s, n, block, stream or None, warmup, iters, per, ctypes.byref(tot)),
+           "kb_bench_stream")
     return list(per), tot.value
 
 

@@ -316,6 +316,32 @@ kb_status kb_bench_triad(float *a, const float *b, const float *c, float s, size
       hs, warmup, iters, ms_per_iter, ms_total);
 }
 
+kb_status kb_bench_stream(int32_t kind, float *a, const float *b, float s, size_t n, int32_t block,
+                          void *stream, int32_t warmup, int32_t iters, float *ms_per_iter,
+                          float *ms_total) {
+  if (kind < KB_STREAM_COPY || kind > KB_STREAM_WRITE) {
+    set_err("kind %d is not a kb_stream_kind", kind);
+    return KB_ERR_INVALID;
+  }
+  if (n < 4 || n % 4 != 0) {
+    set_err("n must be a positive multiple of 4 (got %zu)", n);
+    return KB_ERR_INVALID;
+  }
+  if (((uintptr_t)a | (uintptr_t)b) % 16 != 0) {
+    set_err("a and b must be 16-byte aligned");
+    return KB_ERR_INVALID;
+  }
+  kb_status st = triad_check(a, b, b, n, block);
+  if (st != KB_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  return bench_loop(
+      [&]() {
+        hipError_t e = kb_launch_stream(kind, a, b, s, n, block, hs);
+        return e == hipSuccess ? KB_OK : hip_fail(e, "stream kernel launch");
+      },
+      hs, warmup, iters, ms_per_iter, ms_total);
+}
+
 size_t kb_ceiling_work_size(void) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;

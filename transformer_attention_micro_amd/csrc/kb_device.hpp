@@ -140,6 +140,9 @@ hipError_t kb_launch_fused(const kb_problem &p);
 size_t kb_fused_lds_bytes(const kb_problem &p);
 hipError_t kb_launch_triad(float *a, const float *b, const float *c, float s, size_t n, int block,
                            hipStream_t stream);
+// Copy (kind 1), read-only (2) and write-only (3) bandwidth kernels.
+hipError_t kb_launch_stream(int kind, float *a, const float *b, float s, size_t n, int block,
+                            hipStream_t stream);
 // Compute-ceiling probes (ceiling.hip): waves one launch runs on `cus` CUs,
 // operations it performs, and the launch itself (clk: 2 counters per wave,
 // sink: one float per thread).

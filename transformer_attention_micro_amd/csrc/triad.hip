@@ -22,7 +22,57 @@ __global__ void triad_scalar_kernel(float *__restrict__ a, const float *__restri
     a[i] = fmaf(s, c[i], b[i]);
 }
 
+// Reference bandwidth kernels of the same page ("HBM Bandwidth": copy,
+// read-only and write-only beside the triad), 128-bit accesses, grid-stride.
+__global__ void copy_vec_kernel(float4 *__restrict__ a, const float4 *__restrict__ b, size_t n4) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) a[i] = b[i];
+}
+
+// Read-only: every element is read and summed; the sum is stored (into a,
+// within its n elements) only in the case that it equals `s`, which callers
+// make impossible (NaN), so no bytes are written.
+__global__ void read_vec_kernel(float *__restrict__ a, const float4 *__restrict__ b, float s, size_t n4) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float acc = 0.f;
+  for (size_t i = t; i < n4; i += stride) {
+    const float4 x = b[i];
+    acc += (x.x + x.y) + (x.z + x.w);
+  }
+  if (acc == s && t < 4 * n4) a[t] = acc;
+}
+
+__global__ void write_vec_kernel(float4 *__restrict__ a, float s, size_t n4) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    a[i] = make_float4(s, s, s, s);
+}
+
 }  // namespace
+
+// kind 1 copy (a = b), 2 read (b), 3 write (a = s); n a multiple of 4 and
+// 16-byte aligned operands (checked by the caller).
+hipError_t kb_launch_stream(int kind, float *a, const float *b, float s, size_t n, int block,
+                            hipStream_t stream) {
+  const size_t n4 = n / 4;
+  const size_t blocks = (n4 + block - 1) / block;
+  const unsigned grid = (unsigned)(blocks < (1u << 20) ? blocks : (1u << 20));
+  switch (kind) {
+    case 1:
+      hipLaunchKernelGGL(copy_vec_kernel, dim3(grid), dim3(block), 0, stream, (float4 *)a, (const float4 *)b, n4);
+      break;
+    case 2:
+      hipLaunchKernelGGL(read_vec_kernel, dim3(grid), dim3(block), 0, stream, a, (const float4 *)b, s, n4);
+      break;
+    case 3:
+      hipLaunchKernelGGL(write_vec_kernel, dim3(grid), dim3(block), 0, stream, (float4 *)a, s, n4);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t kb_launch_triad(float *a, const float *b, const float *c, float s, size_t n, int block,
                            hipStream_t stream) {
