@@ -145,6 +145,7 @@ def per_config_table(kb, torch, inputs, stream, cache, iters=10):
 # bound is half of it) and the work per clock per CU of each probe.
 CEIL_PEAK = {"mfma_bf16": 2516.6, "mfma_f32": 157.3, "fma_f32": 157.3 / 2, "exp_f32": None}
 CEIL_PER_CLK_CU = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": None}
+CEIL_MEMORY = ("lds_read", "l1_read", "l2_read")  # read-bandwidth probes, bytes per launch
 
 
 def ceilings(kb, torch, stream, target_ms=40.0):
@@ -153,11 +154,19 @@ def ceilings(kb, torch, stream, target_ms=40.0):
     work = torch.empty(kb.kb_ceiling_work_size(), dtype=torch.uint8, device="cuda")
     cus = kb.kb_device_info()["compute_units"]
     out = {}
-    for kind in ("mfma_bf16", "mfma_f32", "fma_f32", "exp_f32"):
+    for kind in kb.CEILINGS:
         per, _, _ = kb.kb_bench_ceiling(kind, 2000, work.data_ptr(), work.numel(), stream, 1, 1)
         iters = max(1, int(2000 * target_ms / max(per[0], 1e-3)))
         per, ops, mhz = kb.kb_bench_ceiling(kind, iters, work.data_ptr(), work.numel(), stream, 1, 3)
         ms = float(np.median(per))
+        if kind in CEIL_MEMORY:
+            gbs = ops / (ms * 1e-3) / 1e9
+            row = {"unit": "GB/s", "value": round(gbs, 1), "clock_mhz": round(mhz, 0), "ms_per_launch": round(ms, 3),
+                   "iters": iters}
+            if mhz > 0:
+                row["bytes_per_clk_per_cu"] = round(gbs * 1e9 / (cus * mhz * 1e6), 1)
+            out[kind] = row
+            continue
         rate = ops / (ms * 1e-3) / 1e12
         row = {"unit": "Texp/s" if kind == "exp_f32" else "TFLOP/s", "value": round(rate, 2),
                "clock_mhz": round(mhz, 0), "ms_per_launch": round(ms, 3), "iters": iters}

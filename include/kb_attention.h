@@ -146,24 +146,31 @@ kb_status kb_bench_stream(int32_t kind, float *a, const float *b, float s, size_
                           float *ms_total);
 
 /*
- * Compute ceilings (the compute analogue of the triad; method of the
- * micro-benchmark log page, section on compute peaks: independent
+ * Ceiling probes.  Compute kinds (the compute analogue of the triad; method
+ * of the micro-benchmark log page, section on compute peaks: independent
  * instruction chains per thread, dense matrix products with fp32
- * accumulation, the sustained clock recorded beside the result).  One
- * workgroup per CU of eight waves, two per SIMD, each running `iters`
- * iterations of 8 independent chains of one instruction:
+ * accumulation, the sustained clock recorded beside the result) and the
+ * read bandwidth of each on-chip memory level (the measured bandwidth
+ * ceilings of the hierarchical roofline, GPU-Roofline-Python page,
+ * "Bandwidth Ceilings").  One workgroup per CU of eight waves, two per SIMD,
+ * each running `iters` iterations of 8 independent instructions of one kind:
  */
 typedef enum {
   KB_CEIL_MFMA_BF16 = 0, /* v_mfma_f32_32x32x16_bf16: 32768 flops each */
   KB_CEIL_MFMA_F32 = 1,  /* v_mfma_f32_32x32x2f32: 4096 flops each */
   KB_CEIL_FMA_F32 = 2,   /* v_fma_f32 (wave64): 128 flops each */
-  KB_CEIL_EXP_F32 = 3    /* v_exp_f32 (wave64): 64 exponentials each */
+  KB_CEIL_EXP_F32 = 3,   /* v_exp_f32 (wave64): 64 exponentials each */
+  KB_CEIL_LDS_READ = 4,  /* ds_read_b128 over a 64 KiB LDS window: 1024 bytes each */
+  KB_CEIL_L1_READ = 5,   /* 16-byte-per-lane global loads over a 16 KiB slice per
+                            workgroup (vector L1 hits): 1024 bytes each */
+  KB_CEIL_L2_READ = 6    /* the same loads over a 2 MiB region per XCD (L2 hits,
+                            L1 misses): 1024 bytes each */
 } kb_ceiling_kind;
 
 /*
  * Bytes of device work buffer kb_bench_ceiling needs on the current device
- * (per-wave clock counters and one output float per thread); 0 if there is
- * no device.
+ * (per-wave clock counters, one output float per thread and the 16 MiB the
+ * cache probes read); 0 if there is no device.
  */
 size_t kb_ceiling_work_size(void);
 
@@ -171,7 +178,9 @@ size_t kb_ceiling_work_size(void);
  * Timing helper for a ceiling probe, same protocol as kb_bench_attention:
  * `warmup` untimed launches, then `reps` timed ones (ms_per_rep, host,
  * length reps).  *ops_per_launch receives the operations one launch
- * performs (flops for the MFMA and FMA kinds, exponentials for EXP).  If
+ * performs (flops for the MFMA and FMA kinds, exponentials for EXP, bytes
+ * read for the LDS, L1 and L2 kinds).  The cache probes read whatever the
+ * work buffer holds (no initialisation needed).  If
  * clock_mhz is non-NULL it receives the mean shader clock the waves of the
  * last launch ran at (s_memtime over the 100 MHz s_memrealtime).  `work`:
  * device buffer of >= kb_ceiling_work_size() bytes, owned by the caller

@@ -253,7 +253,9 @@ def test_compute_ceiling_probes_run():
     torch = torch_cuda()
     work = torch.empty(kb.kb_ceiling_work_size(), dtype=torch.uint8, device="cuda")
     cus = kb.kb_device_info()["compute_units"]
-    bound = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": 128}  # per clock per CU
+    # per clock per CU (bytes for the memory probes: generous upper bounds)
+    bound = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": 128, "lds_read": 512,
+             "l1_read": 512, "l2_read": 512}
     for kind in kb.CEILINGS:
         per, ops, mhz = kb.kb_bench_ceiling(kind, 200, work.data_ptr(), work.numel(), 0, 1, 2)
         rate = ops / (min(per) * 1e-3)

@@ -347,13 +347,13 @@ size_t kb_ceiling_work_size(void) {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return 0;
-  return (size_t)kb_ceiling_waves(cus) * 2 * sizeof(unsigned long long) + (size_t)cus * 512 * sizeof(float);
+  return kb_ceiling_layout(cus, nullptr, nullptr);
 }
 
 kb_status kb_bench_ceiling(int32_t kind, int32_t iters, void *work, size_t work_bytes, void *stream,
                            int32_t warmup, int32_t reps, float *ms_per_rep, double *ops_per_launch,
                            float *clock_mhz) {
-  if (kind < KB_CEIL_MFMA_BF16 || kind > KB_CEIL_EXP_F32) {
+  if (kind < KB_CEIL_MFMA_BF16 || kind > KB_CEIL_L2_READ) {
     set_err("kind %d is not a kb_ceiling_kind", kind);
     return KB_ERR_INVALID;
   }
@@ -368,18 +368,20 @@ kb_status kb_bench_ceiling(int32_t kind, int32_t iters, void *work, size_t work_
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "multiprocessor count");
   const size_t waves = (size_t)kb_ceiling_waves(cus);
-  const size_t need = waves * 2 * sizeof(unsigned long long) + (size_t)cus * 512 * sizeof(float);
+  size_t sink_off = 0, data_off = 0;
+  const size_t need = kb_ceiling_layout(cus, &sink_off, &data_off);
   if (!work || work_bytes < need) {
     set_err("work buffer of %zu bytes needed (got %zu)", need, work ? work_bytes : (size_t)0);
     return KB_ERR_WORKSPACE;
   }
   unsigned long long *clk = (unsigned long long *)work;
-  float *sink = (float *)(clk + 2 * waves);
+  float *sink = (float *)((unsigned char *)work + sink_off);
+  const unsigned char *data = (const unsigned char *)work + data_off;
   hipStream_t hs = (hipStream_t)stream;
   float total = 0.f;
   st = bench_loop(
       [&]() {
-        hipError_t le = kb_launch_ceiling(kind, cus, iters, clk, sink, hs);
+        hipError_t le = kb_launch_ceiling(kind, cus, iters, clk, sink, data, hs);
         return le == hipSuccess ? KB_OK : hip_fail(le, "ceiling launch");
       },
       hs, warmup, reps, ms_per_rep, &total);

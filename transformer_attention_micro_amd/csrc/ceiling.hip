@@ -1,12 +1,16 @@
-// Compute ceilings: the sustained throughput of the instructions the
-// attention kernels are built from, the compute analogue of the HBM triad.
+// Ceiling probes: the sustained throughput of the instructions the attention
+// kernels are built from (the compute analogue of the HBM triad) and the
+// read bandwidth of each on-chip memory level they stage data through.
 //
-// Method (the micro-benchmark log page, section on compute peaks, its B1
-// and B2 tests): every thread runs several independent chains of one
-// instruction, so no instruction waits for the one before it; the matrix
-// products are dense with fp32 accumulation; and the clock the hardware
-// actually ran at is recorded beside the result, because a datasheet peak
-// assumes the nominal clock and a sustained load does not run there.
+// Method for the compute kinds (the micro-benchmark log page, section on
+// compute peaks, its B1 and B2 tests): every thread runs several independent
+// chains of one instruction, so no instruction waits for the one before it;
+// the matrix products are dense with fp32 accumulation; and the clock the
+// hardware actually ran at is recorded beside the result, because a
+// datasheet peak assumes the nominal clock and a sustained load does not run
+// there.  The memory kinds give the bandwidth ceilings of the hierarchical
+// roofline (the GPU-Roofline-Python page, "Bandwidth Ceilings": measured
+// bandwidths of each cache level beside the datasheet ones).
 //
 // Here one workgroup per CU (a 96 KiB LDS reservation keeps it alone) of
 // eight waves, two per SIMD, loops over
@@ -14,9 +18,20 @@
 //   KB_CEIL_MFMA_F32   v_mfma_f32_32x32x2f32    on 8 independent accumulators
 //   KB_CEIL_FMA_F32    v_fma_f32                on 8 independent chains
 //   KB_CEIL_EXP_F32    v_exp_f32                on 8 independent chains
+//   KB_CEIL_LDS_READ   8 ds_read_b128 per wave per iteration over a 64 KiB
+//                      LDS window (1 KiB contiguous per wave instruction,
+//                      free of bank conflicts)
+//   KB_CEIL_L1_READ    8 global 16-byte-per-lane loads per wave per iteration
+//                      over a 16 KiB slice private to the workgroup, which
+//                      the CU's vector L1 cache holds after the first pass
+//   KB_CEIL_L2_READ    the same loads over a 2 MiB region per XCD (workgroup
+//                      g reads region g mod 8, the XCD it runs on): larger
+//                      than the vector L1, well inside one XCD's 4 MiB L2,
+//                      the workgroups of an XCD spread over the whole region
 // and each wave records the shader clock counter (s_memtime) and the
 // 100 MHz real-time counter (s_memrealtime) around its loop; their ratio is
-// the clock the wave saw.
+// the clock the wave saw.  Every loaded dword feeds an integer sum written
+// to the sink, so no load can be dropped or narrowed.
 #include "kb_attention.h"
 #include "kb_device.hpp"
 
@@ -27,15 +42,35 @@ namespace {
 constexpr int kCeilThreads = 512;
 constexpr int kCeilWaves = kCeilThreads / kWave;
 constexpr int kChains = 8;
+constexpr int kChunk = kWave * 16;                 // bytes one wave's 16-byte-per-lane load moves
+constexpr int kLdsWindowChunks = 64;               // 64 KiB LDS window
+constexpr size_t kL1Slice = 16 * 1024;             // per workgroup
+constexpr size_t kL2Region = 2 * 1024 * 1024;      // per XCD
+constexpr int kL2Groups = (int)(kL2Region / (kChains * kChunk));  // 8-chunk groups per region
+constexpr int kXcdRegions = 8;
+
+__device__ __forceinline__ void consume(const u32x4 v, uint32_t &s0, uint32_t &s1) {
+  s0 += v.x + v.y;
+  s1 += v.z + v.w;
+}
 
 template <int KIND>
 __global__ __launch_bounds__(kCeilThreads) void ceiling_kernel(int iters, float seed,
                                                                unsigned long long *__restrict__ clk,
-                                                               float *__restrict__ sink) {
+                                                               float *__restrict__ sink,
+                                                               const unsigned char *__restrict__ data) {
   __shared__ float reserve[96 * 256];
-  if (iters < 0) reserve[threadIdx.x] = seed;  // never taken; keeps the reservation
   const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  if constexpr (KIND == KB_CEIL_LDS_READ) {
+    // Defined contents for the window the loop reads.
+    for (int i = threadIdx.x; i < kLdsWindowChunks * kChunk / 4; i += kCeilThreads) reserve[i] = seed * i;
+    __syncthreads();
+  } else {
+    if (iters < 0) reserve[threadIdx.x] = seed;  // never taken; keeps the reservation
+  }
   float r = 0.f;
+  uint32_t s0 = 0, s1 = 0;
   const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   if constexpr (KIND == KB_CEIL_MFMA_BF16) {
     bf16x8 a, b;
@@ -72,7 +107,7 @@ __global__ __launch_bounds__(kCeilThreads) void ceiling_kernel(int iters, float 
       for (int c = 0; c < kChains; ++c) x[c] = fmaf(x[c], m, s);
 #pragma unroll
     for (int c = 0; c < kChains; ++c) r += x[c];
-  } else {
+  } else if constexpr (KIND == KB_CEIL_EXP_F32) {
     float x[kChains];
 #pragma unroll
     for (int c = 0; c < kChains; ++c) x[c] = -seed * (lane + c);
@@ -81,14 +116,51 @@ __global__ __launch_bounds__(kCeilThreads) void ceiling_kernel(int iters, float 
       for (int c = 0; c < kChains; ++c) x[c] = exp2_fast(x[c]);
 #pragma unroll
     for (int c = 0; c < kChains; ++c) r += x[c];
+  } else if constexpr (KIND == KB_CEIL_LDS_READ) {
+    const unsigned char *lds = (const unsigned char *)reserve + lane * 16;
+    for (int it = 0; it < iters; ++it) {
+      // First chunk of this wave's 8 (a multiple of 8, at most 56).
+      const unsigned base = ((unsigned)(it + wave) * kChains) & (kLdsWindowChunks - 1);
+      const unsigned char *p = lds + base * kChunk;
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) consume(*(const u32x4 *)(p + c * kChunk), s0, s1);
+    }
+  } else if constexpr (KIND == KB_CEIL_L1_READ) {
+    const unsigned char *g = data + (size_t)blockIdx.x * kL1Slice + lane * 16;
+    for (int it = 0; it < iters; ++it) {
+      const unsigned char *p = g + (size_t)(it & 1) * (kChains * kChunk);
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) consume(*(const u32x4 *)(p + c * kChunk), s0, s1);
+    }
+  } else {
+    const int xcd = blockIdx.x % kXcdRegions, jw = blockIdx.x / kXcdRegions;
+    const unsigned char *g = data + (size_t)xcd * kL2Region + lane * 16;
+    for (int it = 0; it < iters; ++it) {
+      const unsigned group = ((unsigned)it * kCeilWaves + wave + jw * kChains) & (kL2Groups - 1);
+      const unsigned char *p = g + (size_t)group * (kChains * kChunk);
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) consume(*(const u32x4 *)(p + c * kChunk), s0, s1);
+    }
   }
   const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
-  const size_t wave = (size_t)blockIdx.x * kCeilWaves + threadIdx.x / kWave;
+  if constexpr (KIND >= KB_CEIL_LDS_READ) r = __uint_as_float(s0 ^ s1);
+  const size_t w = (size_t)blockIdx.x * kCeilWaves + wave;
   if (lane == 0) {
-    clk[2 * wave] = t1 - t0;
-    clk[2 * wave + 1] = r1 - r0;
+    clk[2 * w] = t1 - t0;
+    clk[2 * w + 1] = r1 - r0;
   }
   sink[(size_t)blockIdx.x * kCeilThreads + threadIdx.x] = r;
+}
+
+static_assert((kL2Groups & (kL2Groups - 1)) == 0, "the L2 region is a power of two of 8-chunk groups");
+static_assert(kLdsWindowChunks * kChunk <= 96 * 256 * 4, "the LDS window fits the reservation");
+static_assert(2 * kChains * kChunk <= (int)kL1Slice, "two 8-chunk halves fit the L1 slice");
+
+template <int KIND>
+void launch_kind(int cus, int iters, unsigned long long *clk, float *sink, const unsigned char *data,
+                 hipStream_t stream) {
+  hipLaunchKernelGGL(ceiling_kernel<KIND>, dim3((unsigned)cus), dim3(kCeilThreads), 0, stream, iters, 1e-3f,
+                     clk, sink, data);
 }
 
 }  // namespace
@@ -99,29 +171,34 @@ double kb_ceiling_ops(int kind, int cus, int iters) {
   const double per_instr = kind == KB_CEIL_MFMA_BF16 ? 2.0 * 32 * 32 * 16
                            : kind == KB_CEIL_MFMA_F32 ? 2.0 * 32 * 32 * 2
                            : kind == KB_CEIL_FMA_F32  ? 2.0 * kWave
-                                                      : 1.0 * kWave;
+                           : kind == KB_CEIL_EXP_F32  ? 1.0 * kWave
+                                                      : (double)kChunk;
   return per_instr * kChains * (double)iters * kb_ceiling_waves(cus);
 }
 
+// Work buffer: per-wave clock counters, one sink float per thread, then the
+// data the cache probes read (4 KiB aligned): an L2 region per XCD or an L1
+// slice per workgroup, whichever is larger.
+size_t kb_ceiling_layout(int cus, size_t *sink_offset, size_t *data_offset) {
+  const size_t sink_off = (size_t)kb_ceiling_waves(cus) * 2 * sizeof(unsigned long long);
+  const size_t data_off = (sink_off + (size_t)cus * kCeilThreads * sizeof(float) + 4095) & ~(size_t)4095;
+  const size_t l2 = (size_t)kXcdRegions * kL2Region, l1 = (size_t)cus * kL1Slice;
+  if (sink_offset) *sink_offset = sink_off;
+  if (data_offset) *data_offset = data_off;
+  return data_off + (l2 > l1 ? l2 : l1);
+}
+
 hipError_t kb_launch_ceiling(int kind, int cus, int iters, unsigned long long *clk, float *sink,
-                             hipStream_t stream) {
-  const dim3 grid((unsigned)cus), block(kCeilThreads);
-  const float seed = 1e-3f;
+                             const unsigned char *data, hipStream_t stream) {
   switch (kind) {
-    case KB_CEIL_MFMA_BF16:
-      hipLaunchKernelGGL(ceiling_kernel<KB_CEIL_MFMA_BF16>, grid, block, 0, stream, iters, seed, clk, sink);
-      break;
-    case KB_CEIL_MFMA_F32:
-      hipLaunchKernelGGL(ceiling_kernel<KB_CEIL_MFMA_F32>, grid, block, 0, stream, iters, seed, clk, sink);
-      break;
-    case KB_CEIL_FMA_F32:
-      hipLaunchKernelGGL(ceiling_kernel<KB_CEIL_FMA_F32>, grid, block, 0, stream, iters, seed, clk, sink);
-      break;
-    case KB_CEIL_EXP_F32:
-      hipLaunchKernelGGL(ceiling_kernel<KB_CEIL_EXP_F32>, grid, block, 0, stream, iters, seed, clk, sink);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case KB_CEIL_MFMA_BF16: launch_kind<KB_CEIL_MFMA_BF16>(cus, iters, clk, sink, data, stream); break;
+    case KB_CEIL_MFMA_F32: launch_kind<KB_CEIL_MFMA_F32>(cus, iters, clk, sink, data, stream); break;
+    case KB_CEIL_FMA_F32: launch_kind<KB_CEIL_FMA_F32>(cus, iters, clk, sink, data, stream); break;
+    case KB_CEIL_EXP_F32: launch_kind<KB_CEIL_EXP_F32>(cus, iters, clk, sink, data, stream); break;
+    case KB_CEIL_LDS_READ: launch_kind<KB_CEIL_LDS_READ>(cus, iters, clk, sink, data, stream); break;
+    case KB_CEIL_L1_READ: launch_kind<KB_CEIL_L1_READ>(cus, iters, clk, sink, data, stream); break;
+    case KB_CEIL_L2_READ: launch_kind<KB_CEIL_L2_READ>(cus, iters, clk, sink, data, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -143,10 +143,12 @@ hipError_t kb_launch_triad(float *a, const float *b, const float *c, float s, si
 // Copy (kind 1), read-only (2) and write-only (3) bandwidth kernels.
 hipError_t kb_launch_stream(int kind, float *a, const float *b, float s, size_t n, int block,
                             hipStream_t stream);
-// Compute-ceiling probes (ceiling.hip): waves one launch runs on `cus` CUs,
-// operations it performs, and the launch itself (clk: 2 counters per wave,
-// sink: one float per thread).
+// Ceiling probes (ceiling.hip): waves one launch runs on `cus` CUs,
+// operations (or bytes) it performs, the work-buffer layout (clock counters,
+// then one sink float per thread, then the data the cache probes read) and
+// the launch itself (clk: 2 counters per wave).
 int kb_ceiling_waves(int cus);
 double kb_ceiling_ops(int kind, int cus, int iters);
+size_t kb_ceiling_layout(int cus, size_t *sink_offset, size_t *data_offset);
 hipError_t kb_launch_ceiling(int kind, int cus, int iters, unsigned long long *clk, float *sink,
-                             hipStream_t stream);
+                             const unsigned char *data, hipStream_t stream);
