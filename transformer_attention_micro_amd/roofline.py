@@ -11,8 +11,9 @@ issue ceiling and one bandwidth ceiling per level.
     python -m transformer_attention_micro_amd.roofline passes DIR        # the rocprofv3 commands
     python -m transformer_attention_micro_amd.roofline report DIR [--svg FILE]
 
-`run` is the program the profiler wraps: each variant `--warmup` + `--launches`
-times at the workload, then calibration kernels whose bytes are known (the HBM read
+`run` is the program the profiler wraps: each variant warmed up (at least
+`--warmup` launches and `--warmup-ms` of them), then `--launches` timed
+launches at the workload; then calibration kernels whose bytes are known (the HBM read
 and write kernels over 1 GiB each, the LDS, L1 and L2 read probes).
 `passes` prints one kernel-trace run and four counter passes of it, each
 within the per-pass counter limits.  `ceilings` measures the bandwidth
@@ -121,8 +122,14 @@ def cmd_run(args) -> int:
         if variant == "naive":
             ws = torch.empty(kb.kb_attention_workspace_size(cfg, "naive"), dtype=torch.uint8, device="cuda")
             c = kb.make_cfg(p.B, p.H, p.S, p.d, p.causal, dt, 0.0, ws.data_ptr(), ws.numel())
-        per, _ = kb.kb_bench_attention(c, *ptrs, variant, stream, args.warmup, args.launches)
-        print(f"[run] {variant} {args.workload}: {args.launches} launches, mean {np.mean(per):.3f} ms", flush=True)
+        # Warm up for at least --warmup-ms: after an idle spell the clock
+        # boosts for a few launches, dips, and takes ~0.2 s of sustained load
+        # to settle where a long run stays.
+        first, _ = kb.kb_bench_attention(c, *ptrs, variant, stream, 0, 1)
+        warm = max(args.warmup, int(math.ceil(args.warmup_ms / max(first[0], 1e-3))))
+        per, _ = kb.kb_bench_attention(c, *ptrs, variant, stream, warm, args.launches)
+        print(f"[run] {variant} {args.workload}: {warm + 1} warmup and {args.launches} timed launches, "
+              f"mean {np.mean(per):.3f} ms", flush=True)
         del ws
         torch.cuda.empty_cache()
     del dev, o
@@ -178,8 +185,14 @@ def cmd_ceilings(args) -> int:
         print(f"[ceilings] {kind}: {ms:.3f} ms at {mhz:.0f} MHz", flush=True)
     del work
     torch.cuda.empty_cache()
-    gbs, block = best_gbs(kb, torch, "read", 2048, (64, 128, 256, 512, 1024), stream, 10, 30)
-    out["levels"]["HBM"] = {"gbs": round(gbs, 1), "block": block, "datasheet_gbs": DATASHEET_HBM_GBS}
+    # HBM: the best of the read-only, write-only and copy kernels (2 GiB
+    # working set, best block size), each kept beside it.
+    hbm = {"datasheet_gbs": DATASHEET_HBM_GBS}
+    for kind in ("read", "write", "copy"):
+        gbs, block = best_gbs(kb, torch, kind, 2048, (64, 128, 256, 512, 1024), stream, 10, 30)
+        hbm[kind] = {"gbs": round(gbs, 1), "block": block}
+    hbm["gbs"] = max(hbm[k]["gbs"] for k in ("read", "write", "copy"))
+    out["levels"]["HBM"] = hbm
     out["valu_gips_nominal"] = round(cus * NOMINAL_MHZ * 1e6 / 1e9, 1)
     text = json.dumps(out, indent=1)
     if args.out:
@@ -394,8 +407,11 @@ def render(met: dict, ct: dict, ceil: dict, checks: dict, cal: dict, cmds: list,
     L.append("")
     L.append("| Level | Measured GB/s | G transactions/s (64 B) | Ridge (VALU instr / transaction) | Probe |")
     L.append("|---|---|---|---|---|")
+    hb = ceil["levels"]["HBM"]
+    hbm_kinds = ", ".join(f"{k} {hb[k]['gbs']:.0f}" for k in ("read", "write", "copy") if k in hb)
     probe = {"LDS": "ds_read_b128, 64 KiB window per CU", "L1": "16 KiB slice per CU",
-             "L2": "2 MiB region per XCD", "HBM": "read kernel, 2 GiB (datasheet 8000 GB/s)"}
+             "L2": "2 MiB region per XCD",
+             "HBM": f"best of the HBM kernels at 2 GiB ({hbm_kinds}; datasheet 8000 GB/s)"}
     for lv in LEVELS:
         L.append(f"| {lv} | {ceil['levels'][lv]['gbs']:.0f} | {ct['tps'][lv] / 1e9:.1f} | {ct['ridge'][lv]:.3g} | "
                  f"{probe[lv]} |")
@@ -491,8 +507,11 @@ def cmd_report(args) -> int:
     met = metrics(trace, passes, cal, int(run_log.get("launches", 0)), int(ceil["compute_units"]),
                   float(ceil["nominal_mhz"]))
     ct = ceiling_table(ceil)
-    cmds = [f"python3 -m transformer_attention_micro_amd.roofline ceilings --out {d}/ceilings.json"]
-    cmds += [c + f" > {d}/run.log" if i == 0 else c for i, c in enumerate(pass_commands(d, args.workload))]
+    # The kernel-trace run goes first, on a GPU that has not just been heated
+    # by the ceiling probes: a hot MI355X runs the same flash launch up to
+    # ~30% slower.
+    cmds = [c + f" > {d}/run.log" if i == 0 else c for i, c in enumerate(pass_commands(d, args.workload))]
+    cmds.insert(1, f"python3 -m transformer_attention_micro_amd.roofline ceilings --out {d}/ceilings.json")
     cmds.append(f"python3 -m transformer_attention_micro_amd.roofline report {d} --workload {args.workload}")
     print(render(met, ct, ceil, checks, cal, cmds, args.title or args.workload))
     if args.svg:
@@ -511,7 +530,8 @@ def main(argv=None) -> int:
     r = sub.add_parser("run")
     r.add_argument("--workload", default="b2h32s8192d128_bf16_causal")
     r.add_argument("--variants", nargs="+", default=["flash", "naive", "fused"])
-    r.add_argument("--warmup", type=int, default=2)
+    r.add_argument("--warmup", type=int, default=10)
+    r.add_argument("--warmup-ms", type=float, default=300.0)
     r.add_argument("--launches", type=int, default=3)
     r.add_argument("--no-calibration", action="store_true")
     c = sub.add_parser("ceilings")
