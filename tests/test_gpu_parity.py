@@ -159,6 +159,35 @@ def test_bf16_output(variant):
         assert np.all(np.abs(got - ref) <= TOL[dtype] + ulp), label
 
 
+# ------------------------------------------- scores that grow along the key axis
+# The bf16 flash kernel takes most tiles without a row maximum, against the
+# running reference, and checks the tile's probability sums instead.  Keys
+# scaled by powers of two (exact in bf16) make later tiles' scores outgrow the
+# reference: by tens of log2 units (the sum check fails and the tile is
+# corrected in place), or by hundreds (the exponentials overflow and the
+# whole query tile is recomputed exactly).
+
+def _growing_keys(d, causal, jump):
+    p = inputs.make_problem(1, 2, 1024, d, inputs.BF16, causal=causal, seed=11)
+    j = np.arange(p.S)
+    if jump:
+        f = np.where(j >= 320, 256.0, 1.0)
+    else:
+        f = 2.0 ** np.minimum(j // 128, 4)
+    p.k[:] = (p.k * f[None, :, None]).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("jump", [False, True])
+def test_flash_scores_outgrowing_the_reference(d, causal, jump):
+    p = _growing_keys(d, causal, jump)
+    o = run(p, "flash").cpu().numpy()
+    want = oracle_full(p)
+    compare(o, want, p.dtype, f"growing-keys/d{d}/{'c' if causal else 'nc'}/{'jump' if jump else 'steps'}")
+
+
 # ---------------------------------------------------------------- invariants through the GPU
 
 @pytest.mark.parametrize("variant", VARIANTS)

@@ -26,6 +26,12 @@
 //    with log2(e) so that one v_exp_f32 (2^x) gives the exponential.
 //  * K/V tiles are double-buffered in LDS: the global loads of tile t+1 are
 //    issued before tile t is computed and written to the other buffer after.
+//  * O and l share a reference m that need not be the running maximum (O / l
+//    does not depend on it in exact arithmetic).  bf16: the first, diagonal,
+//    ragged and last tiles take the exact row maximum; the others take none
+//    and check the sum of their probabilities instead, correcting the tile
+//    in place (or, if the exponentials overflowed, recomputing the query
+//    tile exactly) when the reference proves stale.
 //  * Causal: a workgroup stops at the last key tile its queries can see, a
 //    wave skips the tiles entirely above its rows, and only tiles that cross
 //    the diagonal (or the ragged end of the sequence) evaluate the mask.
@@ -45,6 +51,10 @@ constexpr int kThreads = 256;
 constexpr int kBr = 128;  // queries per workgroup (fp32 kernel)
 // Growth of a row maximum (log2 units) tolerated before rescaling.
 constexpr float kRescaleLog2 = 8.0f;
+// Largest per-lane sum of a steady tile's probabilities, taken against the
+// current reference without a row maximum, accepted without redoing the
+// tile exactly; every accepted probability is then at most this.
+constexpr float kSpecLimit = 4096.0f;
 constexpr int kXcds = 8;
 // s_waitcnt immediate for "vmcnt(0)" with the other counters left alone
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -54,6 +64,7 @@ constexpr int kWaitVm0 = 0x0F70;
 typedef __attribute__((address_space(3))) bf16_t lds_bf16;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Workgroup -> (slice, query tile).  Block L runs on XCD L % 8 (workgroups
 // are dealt round-robin to the XCDs) as that XCD's k-th workgroup, k = L / 8.
@@ -176,6 +187,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   // The LDS ring: kStages K tiles, then kStages V tiles, each BC x D.
   __shared__ __attribute__((aligned(TB))) bf16_t ring[2 * kStages * BC * D];
+  __shared__ int redo_flag;
   auto kst = [&](int j) KB_INLINE { return (lds_bf16 *)(ring + j * BC * D); };
   auto vst = [&](int j) KB_INLINE { return (lds_bf16 *)(ring + (kStages + j) * BC * D); };
 
@@ -219,6 +231,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
   #pragma unroll
     for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
+    bool inexact = false;  // a steady tile's reference was stale beyond repair
 
     const int kend = CAUSAL ? min(S, q0 + kBrB) : S;
     const int ntiles = (kend + BC - 1) / BC;
@@ -383,8 +396,9 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     // maximum and stay below that bound.  O and l use the same reference, so
     // O / l is unchanged in exact arithmetic.  The first tile always moves it
     // (m_run starts at -inf, every row sees a key).  Returns whether it moved;
-    // `alpha` is then the factor for O.
-    auto row_max = [&](float &alpha) KB_INLINE {
+    // `alpha` is then the factor for O.  `thr` is the tolerated growth
+    // (kRescaleLog2, or 0 to move the reference to the maximum).
+    auto row_max = [&](float &alpha, float thr) KB_INLINE {
       float a = -INFINITY, b = -INFINITY;
   #pragma unroll
       for (int v = 0; v < 16; v += 2) {
@@ -392,7 +406,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
         b = fmaxf(fmaxf(b, sc[1][v]), sc[1][v + 1]);
       }
       const float mt = xor32_max(fmaxf(a, b)) * sl2e;
-      const bool grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
+      const bool grow = __builtin_amdgcn_ballot_w64(mt > m_run + thr) != 0;
       const float m_new = grow ? fmaxf(m_run, mt) : m_run;
       alpha = exp2_fast(m_run - m_new);
       l_run *= alpha;
@@ -426,22 +440,27 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     // one instruction stream of NS slots.  Slot i issues the LDS reads of slot
     // i + kPre, MFMA i and its share of the vector work, and the compiler may
     // not move instructions between slots, so the interleave is exactly this:
-    //   MFMA slots  [0, GA)         P V on probability blocks 0-1
-    //               [GA, NPV)       P V on blocks 2-3
-    //               [NPV, NPV+KC)   scores of key half 0 (kc = 0..KC-1)
+    //   MFMA slots  [0, NPV)        P V, probability block cc of t-1 in
+    //                               slots [cc NPV/4, (cc+1) NPV/4)
+    //               [NPV, NPV+KC)   scores of key half 0 of t+1 (kc = 0..KC-1)
     //               [NPV+KC, NS)    scores of key half 1
-    //   vector work row-max steps in the first group, finishing in its last
-    //               slot (m, alpha, l); exponentials and bf16 P of key half 0
-    //               (writing blocks 0-1, already read) in the second group;
-    //               those of half 1 (blocks 2-3) in the third, ahead of the
-    //               MFMAs that overwrite each half; the row sum in the fourth.
+    //   vector work exponentials and bf16 P of key half 0 of t in slots
+    //               [NPV/4, 3 NPV/4), of half 1 in [3 NPV/4, NPV+KC): each
+    //               block of P is rewritten after the MFMAs that read its old
+    //               contents, and each half of the scores is consumed before
+    //               the MFMAs that overwrite it.
+    // A steady tile takes no row maximum: its probabilities are taken against
+    // the current reference m_run, and their per-lane sum, which bounds each
+    // of them, is returned.  If some lane's sum exceeds kSpecLimit (or is not
+    // a number below it: a reference stale by more than the fp32 exponential
+    // can take gives an infinite sum), the caller redoes the tile exactly.
     // The exponentials go two values at a time (two fma, two exp) and the
     // conversion of each pair trails one op behind, so no vector instruction
     // waits on the one just before it.
     auto fused_step = [&](const lds_bf16 *vprev, const lds_bf16 *knext, const lds_bf16 *vnn,
-                          const lds_bf16 *knn, float &alpha, auto &&ld) KB_INLINE {
+                          const lds_bf16 *knn, auto &&ld) KB_INLINE {
       constexpr int NS = NPV + 2 * KC;
-      constexpr int GA = NPV / 2;
+      constexpr int A0 = NPV / 4, B0 = 3 * NPV / 4, E1 = NPV + KC;
       static_assert(NS % kPre == 0 && NPV >= kPre, "fragment ring");
       // Fragment i of this step (i < NS) or of the next one (i >= NS, read
       // from the next step's stages, resident since this step's barrier).
@@ -449,28 +468,8 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
         if (i >= NS) return fetch_first(vnn, knn, i - NS);
         return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
       };
-      float a = -INFINITY, b = -INFINITY, nm = 0.f, ls = 0.f, ls2 = 0.f;
-      bool grow = false;
-      // Row-max step j (0..7): elements 2j, 2j+1 of both halves.
-      auto max_op = [&](int j) KB_INLINE {
-        pin(a);
-        pin(b);
-        a = fmaxf(fmaxf(a, sc[0][2 * j]), sc[0][2 * j + 1]);
-        b = fmaxf(fmaxf(b, sc[1][2 * j]), sc[1][2 * j + 1]);
-        pin(a);
-        pin(b);
-      };
-      auto finish = [&]() KB_INLINE {
-        const float mt = xor32_max(fmaxf(a, b)) * sl2e;
-        grow = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0;
-        const float m_new = grow ? fmaxf(m_run, mt) : m_run;
-        alpha = exp2_fast(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-        nm = -m_new;
-        pin(nm);
-        pin(l_run);
-      };
+      const float nm = -m_run;
+      float ls = 0.f, ls2 = 0.f;
       // bf16 pair p (elements 2p, 2p+1) of half sb -> P, and the pair into the
       // two running sums (plain adds: the packed dot product would occupy the
       // matrix pipeline).
@@ -503,21 +502,15 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
         if (p > 0) cvt_pair(sb, p - 1);
       };
-      // Vector work of slot i.  Group sizes: GA slots for the 8 max steps
-      // (finish in the last), GA slots for the 9 ops of half 0, KC slots for
-      // the 9 ops of half 1; op ranges are spread evenly over each group.
+      // Vector work of slot i: the 9 ops of half 0 spread evenly over
+      // [A0, B0), those of half 1 over [B0, E1).
       auto slot_work = [&](int i) KB_INLINE {
-        if (i < GA) {
-          for (int j = (8 * i) / GA; j < (8 * (i + 1)) / GA; ++j) max_op(j);
-          if (i == GA - 1) finish();
-        } else if (i < NPV) {
-          const int g = i - GA;
-          for (int p = (9 * g) / GA; p < (9 * (g + 1)) / GA; ++p) exp_op(0, p);
-        } else if (i < NPV + KC) {
-          const int g = i - NPV;
-          for (int p = (9 * g) / KC; p < (9 * (g + 1)) / KC; ++p) exp_op(1, p);
-        } else if (i == NPV + KC) {
-          l_run += ls + ls2;
+        if (i >= A0 && i < B0) {
+          const int g = i - A0, n = B0 - A0;
+          for (int p = (9 * g) / n; p < (9 * (g + 1)) / n; ++p) exp_op(0, p);
+        } else if (i >= B0 && i < E1) {
+          const int g = i - B0, n = E1 - B0;
+          for (int p = (9 * g) / n; p < (9 * (g + 1)) / n; ++p) exp_op(1, p);
         }
       };
       bf16x8 pbo[4];
@@ -540,7 +533,56 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
         if (i % LDI == 1 % LDI && i / LDI < 2 * CHW) ld(i / LDI);
         __builtin_amdgcn_sched_barrier(0);
       }
-      return grow;
+      return ls + ls2;
+    };
+
+    // Correction of a steady tile whose sum check failed.  Every probability
+    // of the tile is bf16(2^(x - m_run)); the row's largest one, pmax, shows
+    // how far the reference is below the row's maximum.  If pmax is finite,
+    // the reference moves up by the integer k with pmax 2^-k < 1, and O, l,
+    // the tile's sum and its bf16 probabilities are all multiplied by 2^-k:
+    // exactly, the probabilities by subtracting k from their exponent field
+    // (with unsigned saturation, which flushes the few that fall below the
+    // bf16 range to zero).  The result is what the tile would have given
+    // against the moved reference.  If pmax is infinite (the reference is
+    // stale by more than the fp32 exponential can take) the probabilities
+    // hold no information; returns false and the item is redone exactly.
+    auto spec_fix = [&](float &ls) KB_INLINE {
+      u16x2 mx = {0, 0};
+  #pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const u32x4 wds = __builtin_bit_cast(u32x4, pb[cc]);
+  #pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          // (a bit_cast straight from a vector element would read element 0)
+          const uint32_t wv = wds[w4];
+          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, wv));
+        }
+      }
+      const uint32_t m16 = mx.x > mx.y ? mx.x : mx.y;
+      // Infinity or NaN (exponent field all ones), tested on the bits.
+      if (__builtin_amdgcn_ballot_w64(m16 >= 0x7F80u) != 0) return false;
+      const float pmax = xor32_max(__uint_as_float(m16 << 16));
+      // pmax < 2^e; k = max(e, 0) <= 128.
+      const int k = max((int)(__float_as_uint(pmax) >> 23) - 126, 0);
+      const float alpha = __builtin_amdgcn_ldexpf(1.0f, -k);
+      const u16x2 sub = {(unsigned short)(k << 7), (unsigned short)(k << 7)};
+  #pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        u32x4 wds = __builtin_bit_cast(u32x4, pb[cc]);
+  #pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const uint32_t wv = wds[w4];
+          wds[w4] = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, wv), sub));
+        }
+        pb[cc] = __builtin_bit_cast(bf16x8, wds);
+      }
+      m_run += (float)k;
+      l_run *= alpha;
+      ls *= alpha;
+  #pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+      return true;
     };
 
 
@@ -574,10 +616,12 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
         if (k < CHW) dma(false, k, kst(ST), tk);
         else dma(true, k - CHW, vst((ST + 2) % kStages), tv);
       };
-      float alpha;
-      const bool grow = fused_step(vst((ST + 3) % kStages), kst((ST + 1) % kStages), vst(ST),
-                                   kst((ST + 2) % kStages), alpha, ld);
-      rescale(grow, alpha);
+      const float ls = fused_step(vst((ST + 3) % kStages), kst((ST + 1) % kStages), vst(ST),
+                                  kst((ST + 2) % kStages), ld);
+      float lsum = ls;
+      // An infinite sum (a reference stale beyond the fp32 exponential) counts.
+      if (__builtin_amdgcn_ballot_w64(!(lsum <= kSpecLimit)) != 0 && !spec_fix(lsum)) inexact = true;
+      l_run += lsum;
     };
     // Any step, buffers chosen at run time: the first, the last two of the
     // wave and the idle steps of causal waves that finished early (each wave
@@ -592,7 +636,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
       if (t >= 1 && t - 1 < tw) pv(vst((st + 3) & 3));
       if (t < tw) {
         mask(t);
-        grow = row_max(alpha);
+        grow = row_max(alpha, kRescaleLog2);
         float ls = 0.f;
         probs(0, ls);
         probs(1, ls);
@@ -602,36 +646,57 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
       rescale(grow, alpha);
     };
 
-    // Prologue: K(0..3), V(0..1); every wave computes S^T(0).
-    load_tile(false, kst(0), 0);
-    load_tile(false, kst(1), 1);
-    load_tile(false, kst(2), 2);
-    load_tile(false, kst(3), 3);
-    load_tile(true, vst(0), 0);
-    load_tile(true, vst(1), 1);
-    __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
-    wg_barrier();
-    qk(kst(0));
+    // One pass over the item's key tiles.  The exact pass takes every step
+    // through `general` (a row maximum per tile); it runs only if the fast
+    // pass met a tile whose reference was stale beyond repair.
+    auto pass = [&](bool exact) KB_INLINE {
+      // Prologue: K(0..3), V(0..1); every wave computes S^T(0).
+      load_tile(false, kst(0), 0);
+      load_tile(false, kst(1), 1);
+      load_tile(false, kst(2), 2);
+      load_tile(false, kst(3), 3);
+      load_tile(true, vst(0), 0);
+      load_tile(true, vst(1), 1);
+      __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
+      wg_barrier();
+      qk(kst(0));
 
-    general(0);
-    // Steady steps 1 .. tw - 2: four per iteration, then up to three more.
-    // The first fragments of step 1 are V(0) (stage 0), read ahead here.
-    int t = 1;
+      general(0);
+      int t = 1;
+      if (!exact) {
+        // Steady steps 1 .. tw - 2: four per iteration, then up to three more.
+        // The first fragments of step 1 are V(0) (stage 0), read ahead here.
   #pragma unroll
-    for (int i = 0; i < kPre; ++i) buf[i] = fetch_first(vst(0), kst(2), i);
-    for (; t + 3 <= tw - 2; t += 4) {
-      steady(std::integral_constant<int, 1>{}, t);
-      steady(std::integral_constant<int, 2>{}, t + 1);
-      steady(std::integral_constant<int, 3>{}, t + 2);
-      steady(std::integral_constant<int, 0>{}, t + 3);
-    }
-    if (t <= tw - 2) steady(std::integral_constant<int, 1>{}, t++);
-    if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
-    if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
-    for (; t <= ntiles; ++t) general(t);
+        for (int i = 0; i < kPre; ++i) buf[i] = fetch_first(vst(0), kst(2), i);
+        for (; t + 3 <= tw - 2; t += 4) {
+          steady(std::integral_constant<int, 1>{}, t);
+          steady(std::integral_constant<int, 2>{}, t + 1);
+          steady(std::integral_constant<int, 3>{}, t + 2);
+          steady(std::integral_constant<int, 0>{}, t + 3);
+        }
+        if (t <= tw - 2) steady(std::integral_constant<int, 1>{}, t++);
+        if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
+        if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
+      }
+      for (; t <= ntiles; ++t) general(t);
+      // No tile load may still be writing this workgroup's LDS when it ends.
+      __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
+    };
 
-    // No tile load may still be writing this workgroup's LDS when it ends.
-    __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
+    // Cleared before the prologue's barrier; set by any wave whose fast pass
+    // went inexact; read by all after the barrier that ends the pass.
+    if (tid == 0) redo_flag = 0;
+    pass(false);
+    if (inexact && lane == 0) redo_flag = 1;
+    wg_barrier();
+    if (redo_flag != 0) {
+  #pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
+      m_run = -INFINITY;
+      l_run = 0.f;
+      inexact = false;
+      pass(true);
+    }
 
     const float inv = 1.f / xor32_sum(l_run);
     if (q < S) {
