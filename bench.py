@@ -4,7 +4,10 @@
 
 One step is one attention forward pass (kb_attention, variant flash) over the
 workload B=2, H=32, S=8192, d=128, bf16 inputs, causal mask, fp32 output,
-with Q, K, V already resident in HBM.  The K timed steps are bracketed by
+with Q, K, V already resident in HBM.  The default warmup (200 launches,
+~0.2 s) outlasts the clock transient of an MI355X coming out of idle (a few
+fast launches, a dip of up to ~30 %, then ~0.1 s of recovery), so the timed
+steps measure sustained throughput.  The K timed steps are bracketed by
 torch.cuda.synchronize() on both sides; inside, kb_bench_attention records a
 hipEvent between consecutive launches on the launch stream, which gives the
 per-launch kernel time used for the roofline fraction.
@@ -22,8 +25,9 @@ The JSON line also carries:
                 working set (best of the same sweep);
   variants      naive and fused on the same workload (a few timed calls);
   per_config    flash on every configured workload (the metric is quoted per
-                (B, H, S, d), causal or not): mean hipEvent time per launch,
-                TFLOP/s and the fraction of the dtype's MFMA peak;
+                (B, H, S, d), causal or not), each warmed up for ~0.3 s:
+                mean hipEvent time per launch, TFLOP/s and the fraction of
+                the dtype's MFMA peak;
   ceilings      sustained compute ceilings (kb_bench_ceiling: bf16 and fp32
                 MFMA, fp32 FMA, exp) with the shader clock the probe ran at,
                 the compute analogue of the triad.
@@ -50,8 +54,8 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="b2h32s8192d128_bf16_causal")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -116,9 +120,10 @@ def cpu_baseline(p, o_gpu, budget_s, seed=1234):
     }
 
 
-def per_config_table(kb, torch, inputs, stream, cache, iters=10):
+def per_config_table(kb, torch, inputs, stream, cache, iters=20, warm_ms=300.0):
     """Flash on every configured workload (seeded inputs per the recipe; the
-    S=8192 workload also without the mask)."""
+    S=8192 workload also without the mask), each warmed up for at least
+    warm_ms so the row is not measured inside a clock transient."""
     rows = []
     for name in inputs.WORKLOADS:
         p = cache[name] if name in cache else inputs.workload(name)
@@ -127,8 +132,10 @@ def per_config_table(kb, torch, inputs, stream, cache, iters=10):
         dt = kb.KB_BF16 if p.dtype == inputs.BF16 else kb.KB_F32
         for causal in ([True, False] if name == "b2h32s8192d128_bf16_causal" else [p.causal]):
             cfg = kb.make_cfg(p.B, p.H, p.S, p.d, causal, dt)
-            per, _ = kb.kb_bench_attention(cfg, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                           "flash", stream, 3, iters)
+            ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
+            first, _ = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, 0, 1)
+            warm = max(3, int(np.ceil(warm_ms / max(first[0], 1e-3))))
+            per, _ = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, warm, iters)
             ms = float(np.mean(per))
             fl = kb.attention_flops(p.B, p.H, p.S, p.d, causal)
             tf = fl / (ms * 1e-3) / 1e12
