@@ -275,7 +275,8 @@ def main():
         "dtype": p.dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "B": p.B, "H": p.H, "S": p.S, "d": p.d,
-                   "causal": p.causal, "variant": "flash", "out": "f32", "flops_per_step": flops},
+                   "causal": p.causal, "variant": "flash", "out": "f32", "flops_per_step": flops,
+                   "seed": p.seed, "inputs_sha256": p.sha256()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_min": round(float(np.min(per)), 4),

@@ -61,8 +61,9 @@ def sampled_check(p, variant, label, seed=0):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_b1h1s64d32_f32(variant):
-    p = workload("b1h1s64d32_f32")
-    full_check(p, variant, f"b1h1s64d32_f32/{variant}")
+    for seed in (0, 1, 2):
+        p = workload("b1h1s64d32_f32", seed=seed)
+        full_check(p, variant, f"b1h1s64d32_f32/seed{seed}/{variant}")
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -76,8 +77,9 @@ def test_b1h8s512d64_f32(variant, causal):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_b4h16s2048d64_bf16_causal(variant):
-    p = workload("b4h16s2048d64_bf16_causal")
-    full_check(p, variant, f"b4h16s2048d64_bf16_causal/{variant}")
+    for seed in (0, 1, 2):
+        p = workload("b4h16s2048d64_bf16_causal", seed=seed)
+        full_check(p, variant, f"b4h16s2048d64_bf16_causal/seed{seed}/{variant}")
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -85,6 +87,18 @@ def test_b4h16s2048d64_bf16_causal(variant):
 def test_b2h32s8192d128(variant, name):
     p = workload(name)
     sampled_check(p, variant, f"{name}/{variant}")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+@pytest.mark.parametrize("name", ["b2h32s8192d128_bf16_causal", "b2h32s8192d128_bf16_causal_q8"])
+def test_b2h32s8192d128_flash_more_seeds(name, seed):
+    """The measured kernel on two more input draws (not cached: 768 MiB each)."""
+    p = inputs.workload(name, seed=seed)
+    rows = sample_rows(p.S, p.BH, seed)
+    want = oracle_rows(p, rows)
+    o = run(p, "flash").cpu().numpy().reshape(p.BH * p.S, p.d)
+    assert np.all(np.isfinite(o)), "non-finite output somewhere"
+    compare(o[rows], want, p.dtype, f"{name}/seed{seed}/flash")
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
