@@ -181,8 +181,8 @@ def test_bf16_output(variant):
 # corrected in place), or by hundreds (the exponentials overflow and the
 # whole query tile is recomputed exactly).
 
-def _growing_keys(d, causal, jump):
-    p = inputs.make_problem(1, 2, 1024, d, inputs.BF16, causal=causal, seed=11)
+def _growing_keys(d, causal, jump, S=1024):
+    p = inputs.make_problem(1, 2, S, d, inputs.BF16, causal=causal, seed=11)
     j = np.arange(p.S)
     if jump:
         f = np.where(j >= 320, 256.0, 1.0)
@@ -192,14 +192,17 @@ def _growing_keys(d, causal, jump):
     return p
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("jump", [False, True])
-def test_flash_scores_outgrowing_the_reference(d, causal, jump):
-    p = _growing_keys(d, causal, jump)
+@pytest.mark.parametrize("S", [1024, 1000])
+def test_flash_scores_outgrowing_the_reference(d, causal, jump, S):
+    """S = 1000 adds a ragged last tile and a last query tile with rows past
+    the sequence end."""
+    p = _growing_keys(d, causal, jump, S)
     o = run(p, "flash").cpu().numpy()
     want = oracle_full(p)
-    compare(o, want, p.dtype, f"growing-keys/d{d}/{'c' if causal else 'nc'}/{'jump' if jump else 'steps'}")
+    compare(o, want, p.dtype, f"growing-keys/S{S}/d{d}/{'c' if causal else 'nc'}/{'jump' if jump else 'steps'}")
 
 
 # ---------------------------------------------------------------- invariants through the GPU
