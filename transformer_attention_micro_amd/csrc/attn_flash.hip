@@ -542,9 +542,10 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     // the reference moves up by the integer k with pmax 2^-k < 1, and O, l,
     // the tile's sum and its bf16 probabilities are all multiplied by 2^-k:
     // exactly, the probabilities by subtracting k from their exponent field
-    // (with unsigned saturation, which flushes the few that fall below the
-    // bf16 range to zero).  The result is what the tile would have given
-    // against the moved reference.  If pmax is infinite (the reference is
+    // (with unsigned saturation: the few whose exponent would drop to zero
+    // or below become zero or a denormal, all under 2^-126 against the row's
+    // largest, which the moved reference makes < 1).  The result is what the
+    // tile would have given against the moved reference.  If pmax is infinite (the reference is
     // stale by more than the fp32 exponential can take) the probabilities
     // hold no information; returns false and the item is redone exactly.
     auto spec_fix = [&](float &ls) KB_INLINE {
