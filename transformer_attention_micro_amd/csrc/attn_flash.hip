@@ -39,6 +39,7 @@
 //    (batch, head) slice, so with round-robin dispatch over the 8 XCDs all
 //    query tiles of a slice share one XCD's L2.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "kb_device.hpp"
@@ -867,17 +868,18 @@ __global__ __launch_bounds__(kThreads) void flash_f32_kernel(const float *__rest
 // Work units per slice of the persistent bf16 schedule.
 constexpr int causal_units(int nqt, bool causal) { return causal ? (nqt + 1) / 2 : nqt; }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; callers on
+// several host threads may race to fill the cache with the same value).
 int cu_count() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] <= 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 template <int D, bool CAUSAL>
