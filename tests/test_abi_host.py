@@ -168,3 +168,25 @@ def test_stream_argument_checks():
     assert lib.kb_bench_stream(1, FAKE, FAKE + 64, 1.0, 1024, 256, None, 0, 2, per, ct.byref(tot)) == 1
     assert lib.kb_bench_stream(1, *ok, 1.0, 1024, 100, None, 0, 2, per, ct.byref(tot)) == 1   # block
     assert lib.kb_bench_stream(1, None, FAKE, 1.0, 1024, 256, None, 0, 2, per, ct.byref(tot)) == 1
+
+
+def test_last_error_is_per_thread():
+    """The error text lives in thread-local storage: a failing call on one
+    host thread leaves another thread's message alone."""
+    import threading
+
+    lib = kb.lib()
+    assert lib.kb_attention(None, FAKE, FAKE, FAKE, FAKE, 2, None) == 1
+    mine = lib.kb_last_error()
+    assert b"cfg" in mine
+    seen = {}
+
+    def other():
+        assert status_of(cfg(dim=48)) == 2  # unsupported head dimension
+        seen["msg"] = lib.kb_last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] != mine and b"48" in seen["msg"]
+    assert lib.kb_last_error() == mine

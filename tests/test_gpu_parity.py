@@ -256,6 +256,40 @@ def test_repeat_runs_are_bit_identical(variant):
     assert np.array_equal(a, b)
 
 
+def test_concurrent_host_threads_match_serial():
+    """Four host threads, each on its own stream, run flash on the same
+    inputs at once (the ctypes call releases the interpreter lock); every
+    output equals the serial one bit for bit."""
+    import threading
+
+    torch = torch_cuda()
+    p = inputs.make_problem(1, 4, 1024, 128, inputs.BF16, causal=True, seed=5)
+    q, k, v = to_device(p)
+    ref = nan_output(p)
+    kb.attention(q, k, v, ref, causal=True, variant="flash", heads=p.H)
+    torch.cuda.synchronize()
+    outs = [nan_output(p) for _ in range(4)]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    errors = []
+
+    def work(i):
+        try:
+            for _ in range(5):
+                kb.attention(q, k, v, outs[i], causal=True, variant="flash", heads=p.H, stream=streams[i])
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
 def test_variants_agree_with_each_other():
     p = inputs.make_problem(1, 4, 1024, 64, inputs.F32, causal=True, seed=7)
     outs = {v: run(p, v).cpu().numpy() for v in VARIANTS}
