@@ -19,7 +19,9 @@ The JSON line also carries:
                 profiles/ (null if the kernel changed since it was taken);
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded,
                 seeded sample of the same workload's query rows (also used
-                to check the GPU output on those rows);
+                to check the GPU output on those rows); small_configs: the
+                oracle on every row of each workload with S <= 2048, on all
+                threads and on one, beside the GPU's time and its error;
   triad         the HBM triad calibration (best of a block-size sweep);
   hbm_reference copy, read-only and write-only kernels at the same 2 GiB
                 working set (best of the same sweep);
@@ -118,6 +120,40 @@ def cpu_baseline(p, o_gpu, budget_s, seed=1234):
                   f"{t_used:.1f} s; throughput scaled by the rows' algorithmic FLOPs",
         "max_abs_err_vs_gpu_on_sample": max(errs),
     }
+
+
+def cpu_small_configs(kb, torch, inputs, stream):
+    """The fp64 oracle on every row of the small workloads (S <= 2048), with
+    all the host threads and with one, beside one flash launch on the GPU of
+    the same inputs: oracle time, its FLOP rate, the GPU's kernel time and
+    speed-up, and the max-abs and relative-L2 error of the GPU output."""
+    import oracle
+    out = []
+    for name, spec in inputs.WORKLOADS.items():
+        if spec["S"] > 2048:
+            continue
+        p = inputs.workload(name)
+        q, k, v = device_tensors(p, torch)
+        o = torch.empty((p.BH, p.S, p.d), dtype=torch.float32, device="cuda")
+        dt = kb.KB_BF16 if p.dtype == inputs.BF16 else kb.KB_F32
+        cfg = kb.make_cfg(p.B, p.H, p.S, p.d, p.causal, dt)
+        per, _ = kb.kb_bench_attention(cfg, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), "flash",
+                                       stream, 20, 20)
+        got = o.cpu().numpy().astype(np.float64)
+        flops = kb.attention_flops(p.B, p.H, p.S, p.d, p.causal)
+        row = {"workload": name, "gpu_kernel_ms_median": round(float(np.median(per)), 4)}
+        for label, nt in (("all_threads", oracle.default_threads()), ("one_thread", 1)):
+            t0 = time.perf_counter()
+            ref = oracle.sdpa(p.q, p.k, p.v, causal=p.causal, nthreads=nt)
+            sec = time.perf_counter() - t0
+            row[label] = {"threads": nt, "seconds": round(sec, 4), "gflops": round(flops / sec / 1e9, 2)}
+        row["gpu_speedup_vs_all_threads"] = round(row["all_threads"]["seconds"] * 1e3 / row["gpu_kernel_ms_median"], 1)
+        row["max_abs_err"] = float(np.max(np.abs(got - ref)))
+        row["rel_l2_err"] = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        out.append(row)
+        del q, k, v, o
+        torch.cuda.empty_cache()
+    return out
 
 
 def per_config_table(kb, torch, inputs, stream, cache, iters=20, warm_ms=300.0):
@@ -332,6 +368,7 @@ def main():
         torch.cuda.synchronize()
         o_host = o.cpu().numpy().reshape(p.BH * p.S, p.d).astype(np.float64)
         result["cpu_baseline"] = cpu_baseline(p, o_host, args.cpu_seconds)
+        result["cpu_baseline"]["small_configs"] = cpu_small_configs(kb, torch, inputs, stream)
 
     print(json.dumps(result), flush=True)
     return 0
