@@ -23,9 +23,15 @@
 //    rounded to bf16 (round to nearest even) for P V.  fp32 inputs: fp32
 //    MFMA (32x32x2) and fp32 probabilities throughout.
 //  * The logit scale is applied in fp32 to the fp32 dot products, folded
-//    with log2(e) so that one v_exp_f32 (2^x) gives the exponential.
-//  * K/V tiles are double-buffered in LDS: the global loads of tile t+1 are
-//    issued before tile t is computed and written to the other buffer after.
+//    with log2(e) so that one v_exp_f32 (2^x) gives the exponential.  (It is
+//    not folded into Q: rounding the scaled Q to bf16 errs in proportion to
+//    the logits, several times the bf16 tolerance at large logits.)
+//  * bf16: K/V tiles go global->LDS by direct loads into a 4-stage ring, and
+//    a persistent grid walks an XCD-aware list of query tiles.  The row sums
+//    of the steady tiles are taken by small MFMAs from the bf16
+//    probabilities, which keeps an add per score off the vector ALU.
+//    fp32: K/V tiles are double-buffered in LDS through registers (the loads
+//    of tile t+1 are issued before tile t is computed) on a dispatched grid.
 //  * O and l share a reference m that need not be the running maximum (O / l
 //    does not depend on it in exact arithmetic).  bf16: the first, diagonal,
 //    ragged and last tiles take the exact row maximum; the others take none
@@ -35,9 +41,9 @@
 //  * Causal: a workgroup stops at the last key tile its queries can see, a
 //    wave skips the tiles entirely above its rows, and only tiles that cross
 //    the diagonal (or the ragged end of the sequence) evaluate the mask.
-//    Heavy (late) query tiles are dispatched first, and blockIdx.x is the
-//    (batch, head) slice, so with round-robin dispatch over the 8 XCDs all
-//    query tiles of a slice share one XCD's L2.
+//    The query tiles of a (batch, head) slice all run on one XCD, so they
+//    share its L2; causal work is balanced by pairing heavy and light query
+//    tiles (bf16) or by dispatching heavy tiles first (fp32).
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -146,7 +152,9 @@ __device__ __forceinline__ void pin(T &x) {
 // keeps the matrix core busy.  Per 64-key tile step t a wave has three pieces of
 // work:
 //   O^T += V(t-1)^T P(t-1)^T    (MFMA, V from LDS, P from registers)
-//   softmax of tile t           (vector ALU: row max, exponentials, bf16 P)
+//   softmax of tile t           (vector ALU: exponentials, bf16 P; a row
+//                                max only on the first, diagonal and last
+//                                tiles)
 //   S^T(t+1) = K(t+1) Q^T       (MFMA, K from LDS)
 // and its instruction stream interleaves them, so the vector ALU works in
 // the shadow of the matrix core (a wave keeps issuing independent
@@ -357,6 +365,20 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     // 16 cc + {4h..4h+3, 8+4h..8+4h+3} (the B operand layout of P^T).
     f32x16 sc[2];
     bf16x8 pb[4];
+    // Row sums by MFMA: v_mfma_f32_16x16x32_bf16 with B = a block of P
+    // (lane l's eight values read as column l % 16, contraction slots
+    // 8 (l / 16) .. +7) and this constant A (lane l holds row l % 16 over
+    // the same slots): 1 where the lane's slot group l / 16 equals its
+    // row / 4, else 0.  Output row i then sums the eight B values of lane
+    // group i / 4 in column j, and lane l holds rows 4 (l / 16) .. +3 of
+    // column l % 16: every lane receives, four times, the sum of its own
+    // eight probabilities, in fp32.
+    bf16x8 sum_a;
+    {
+      const bf16_t one = (bf16_t)(((lane >> 4) == ((lane & 15) >> 2)) ? 1.0f : 0.0f);
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) sum_a[e] = one;
+    }
 
     // Scores of the next tile into sc; each half starts once the
     // probabilities of the old contents (pb[2 half], pb[2 half + 1]) exist.
@@ -451,10 +473,13 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     //               contents, and each half of the scores is consumed before
     //               the MFMAs that overwrite it.
     // A steady tile takes no row maximum: its probabilities are taken against
-    // the current reference m_run, and their per-lane sum, which bounds each
-    // of them, is returned.  If some lane's sum exceeds kSpecLimit (or is not
-    // a number below it: a reference stale by more than the fp32 exponential
-    // can take gives an infinite sum), the caller redoes the tile exactly.
+    // the current reference m_run, and the per-lane sum of their bf16 values,
+    // which bounds each of them, is returned.  It is taken by four row-sum
+    // MFMAs, each issued in the slot after its probability block is complete,
+    // so the vector ALU does no add per score.  If some lane's sum exceeds
+    // kSpecLimit (or is not a number below it: a reference stale by more
+    // than the fp32 exponential can take gives an infinite probability),
+    // the caller corrects the tile or redoes the item exactly.
     // The exponentials go two values at a time (two fma, two exp) and the
     // conversion of each pair trails one op behind, so no vector instruction
     // waits on the one just before it.
@@ -470,20 +495,14 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
         return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
       };
       const float nm = -m_run;
-      float ls = 0.f, ls2 = 0.f;
-      // bf16 pair p (elements 2p, 2p+1) of half sb -> P, and the pair into the
-      // two running sums (plain adds: the packed dot product would occupy the
-      // matrix pipeline).
+      f32x4 lsv = f32x4{};
+      // bf16 pair p (elements 2p, 2p+1) of half sb -> P.
       auto cvt_pair = [&](int sb, int p) KB_INLINE {
         bf16x2 pr = {(bf16_t)sc[sb][2 * p], (bf16_t)sc[sb][2 * p + 1]};
         pin(pr);
         const int cc = 2 * sb + p / 4, e = p % 4;
         pb[cc][2 * e] = pr[0];
         pb[cc][2 * e + 1] = pr[1];
-        ls += sc[sb][2 * p];
-        ls2 += sc[sb][2 * p + 1];
-        pin(ls);
-        pin(ls2);
       };
       // Exponential op p (0..8) of half sb: exponentials of pair p (p < 8),
       // then the conversion of pair p - 1.
@@ -514,6 +533,16 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
           for (int p = (9 * g) / n; p < (9 * (g + 1)) / n; ++p) exp_op(1, p);
         }
       };
+      // Slot of exponential op p of half sb (as slot_work places it), and the
+      // slot after the one completing probability block cc.
+      constexpr auto op_slot = [](int sb, int p) {
+        const int st = sb == 0 ? A0 : B0, n = sb == 0 ? B0 - A0 : E1 - B0;
+        for (int g = 0; g < n; ++g)
+          if ((9 * g) / n <= p && p < (9 * (g + 1)) / n) return st + g;
+        return -1;
+      };
+      constexpr auto sum_slot = [op_slot](int cc) { return op_slot(cc / 2, 4 * (cc % 2) + 4) + 1; };
+      static_assert(sum_slot(3) < NS, "row sums inside the step");
       bf16x8 pbo[4];
   #pragma unroll
       for (int cc = 0; cc < 4; ++cc) pbo[cc] = pb[cc];
@@ -528,27 +557,33 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
           sc[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : sc[half]);
         }
         slot_work(i);
+  #pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          if (i == sum_slot(cc)) lsv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sum_a, pb[cc], lsv, 0, 0, 0);
         // This step's 2 CHW tile loads, spread evenly over the slots so the
         // CU's load pipeline never backs up into the instruction stream.
         constexpr int LDI = NS / (2 * CHW);
         if (i % LDI == 1 % LDI && i / LDI < 2 * CHW) ld(i / LDI);
         __builtin_amdgcn_sched_barrier(0);
       }
-      return ls + ls2;
+      return lsv[0];
     };
 
     // Correction of a steady tile whose sum check failed.  Every probability
     // of the tile is bf16(2^(x - m_run)); the row's largest one, pmax, shows
     // how far the reference is below the row's maximum.  If pmax is finite,
-    // the reference moves up by the integer k with pmax 2^-k < 1, and O, l,
-    // the tile's sum and its bf16 probabilities are all multiplied by 2^-k:
-    // exactly, the probabilities by subtracting k from their exponent field
-    // (with unsigned saturation: the few whose exponent would drop to zero
-    // or below become zero or a denormal, all under 2^-126 against the row's
-    // largest, which the moved reference makes < 1).  The result is what the
-    // tile would have given against the moved reference.  If pmax is infinite (the reference is
-    // stale by more than the fp32 exponential can take) the probabilities
-    // hold no information; returns false and the item is redone exactly.
+    // the reference moves up by the integer k with pmax 2^-k < 1, and O, l
+    // and the tile's bf16 probabilities are multiplied by 2^-k: exactly, the
+    // probabilities by subtracting k from their exponent field (with
+    // unsigned saturation: the few whose exponent would drop to zero or
+    // below become zero or a denormal, all under 2^-126 against the row's
+    // largest, which the moved reference makes < 1).  The tile's sum is then
+    // taken again from the corrected probabilities (scaling the old one
+    // would keep an fp32 overflow of the sum of finite values).  The result
+    // is what the tile would have given against the moved reference.  If
+    // pmax is infinite (the reference is stale by more than the fp32
+    // exponential can take) the probabilities hold no information; returns
+    // false and the item is redone exactly.
     auto spec_fix = [&](float &ls) KB_INLINE {
       u16x2 mx = {0, 0};
   #pragma unroll
@@ -579,9 +614,13 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
         pb[cc] = __builtin_bit_cast(bf16x8, wds);
       }
+      // The tile's sum from the corrected probabilities (each now below 1).
+      f32x4 s4 = f32x4{};
+  #pragma unroll
+      for (int cc = 0; cc < 4; ++cc) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sum_a, pb[cc], s4, 0, 0, 0);
+      ls = s4[0];
       m_run += (float)k;
       l_run *= alpha;
-      ls *= alpha;
   #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
       return true;
@@ -621,8 +660,13 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
       const float ls = fused_step(vst((ST + 3) % kStages), kst((ST + 1) % kStages), vst(ST),
                                   kst((ST + 2) % kStages), ld);
       float lsum = ls;
-      // An infinite sum (a reference stale beyond the fp32 exponential) counts.
-      if (__builtin_amdgcn_ballot_w64(!(lsum <= kSpecLimit)) != 0 && !spec_fix(lsum)) inexact = true;
+      // The check compares bit patterns (the sum is never negative): it also
+      // fails a NaN sum, which the row-sum MFMA gives every lane of a wave in
+      // which some probability is infinite (its zero weights times infinity),
+      // and which a float comparison, compiled here without NaN semantics,
+      // could let through.
+      if (__builtin_amdgcn_ballot_w64(__float_as_uint(lsum) > __float_as_uint(kSpecLimit)) != 0 && !spec_fix(lsum))
+        inexact = true;
       l_run += lsum;
     };
     // Any step, buffers chosen at run time: the first, the last two of the
