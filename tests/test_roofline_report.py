@@ -57,6 +57,7 @@ def result_dir(tmp_path):
             SOFTMAX: {"SQ_INSTS": 1e9, "SQ_INSTS_VALU": 8e8, "SQ_INSTS_MFMA": 0.0, "SQ_INSTS_LDS": 3e7}}
     # flash: LDS 64 B x 2e8, L1 accesses 1e8 (x 64 B), L2 sectors 2e8 (x 32 B), HBM 1e6 KiB fetched (x2), 2.5e5 written
     mem = {FLASH: {"SQ_INSTS_LDS_LOAD_BANDWIDTH": 1.5e8, "SQ_INSTS_LDS_STORE_BANDWIDTH": 5e7,
+                   "SQ_VALU_MFMA_BUSY_CYCLES": 3e7 * 30,
                    "TCP_TOTAL_CACHE_ACCESSES_sum": 1e8, "TCC_READ_SECTORS_sum": 1.5e8, "TCC_WRITE_SECTORS_sum": 5e7},
            SOFTMAX: {"SQ_INSTS_LDS_LOAD_BANDWIDTH": 1e7, "SQ_INSTS_LDS_STORE_BANDWIDTH": 0.0,
                      "TCP_TOTAL_CACHE_ACCESSES_sum": 4e8, "TCC_READ_SECTORS_sum": 4e8, "TCC_WRITE_SECTORS_sum": 4e8}}
@@ -135,7 +136,10 @@ def test_metrics_follow_the_definitions(result_dir):
         assert f["intensity"][lv] == pytest.approx(2e8 / f["tx"][lv])
     assert f["gips_valu"] == pytest.approx(2e8 / 1e6)
     assert f["gips_all"] == pytest.approx(3e8 / 1e6)
-    assert f["mfma_pipe"] == pytest.approx(3e7 * 32 / (4 * 256 * 2.4e9 * 1e-3))
+    # measured matrix-pipe clocks when the counter is there, else 32 per MFMA
+    assert f["mfma_busy_measured"]
+    assert f["mfma_pipe"] == pytest.approx(3e7 * 30 / (4 * 256 * 2.4e9 * 1e-3))
+    assert not met["naive 2/3 softmax"]["mfma_busy_measured"]
     s = met["naive 2/3 softmax"]
     assert s["gbs"]["HBM"] == pytest.approx((6.25e6 * 2 + 1.25e7) * 1024 / 2e-3 / 1e9)
 

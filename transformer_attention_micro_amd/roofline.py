@@ -57,8 +57,9 @@ import numpy as np
 PASSES = {
     "inst": ["SQ_INSTS", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_SMEM", "SQ_INSTS_LDS",
              "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR"],
-    "mem": ["SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_LDS_STORE_BANDWIDTH", "TCP_TOTAL_CACHE_ACCESSES_sum",
-            "TCP_TCC_READ_REQ_sum", "TCP_TCC_WRITE_REQ_sum", "TCC_READ_SECTORS_sum", "TCC_WRITE_SECTORS_sum"],
+    "mem": ["SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_LDS_STORE_BANDWIDTH", "SQ_VALU_MFMA_BUSY_CYCLES",
+            "TCP_TOTAL_CACHE_ACCESSES_sum", "TCP_TCC_READ_REQ_sum", "TCP_TCC_WRITE_REQ_sum", "TCC_READ_SECTORS_sum",
+            "TCC_WRITE_SECTORS_sum"],
     "fetch": ["FETCH_SIZE"],
     "write": ["WRITE_SIZE"],
 }
@@ -299,9 +300,13 @@ def metrics(trace: dict, passes: dict, calib: dict, timed: int = 0, cus: int = 2
              "lds_insts": c("SQ_INSTS_LDS"), "vmem_rd": c("SQ_INSTS_VMEM_RD"), "vmem_wr": c("SQ_INSTS_VMEM_WR"),
              "tx": tx}
         m["gips_valu"] = m["valu"] / (t_ns * 1e-9) / 1e9
-        # 32x32 MFMAs hold a SIMD's matrix pipe 32 clocks (16 for the f32 ones;
-        # both kernels that use them are dominated by the bf16 32x32x16 form).
-        m["mfma_pipe"] = m["mfma"] * 32 / (4 * cus * mhz * 1e6 * t_ns * 1e-9)
+        # Matrix-pipe clocks summed over the SIMDs, measured; without that
+        # counter, 32 per MFMA (the bf16 32x32x16 form; a 16x16x32 takes 16).
+        busy = c("SQ_VALU_MFMA_BUSY_CYCLES")
+        m["mfma_busy_measured"] = not math.isnan(busy)
+        if not m["mfma_busy_measured"]:
+            busy = m["mfma"] * 32
+        m["mfma_pipe"] = busy / (4 * cus * mhz * 1e6 * t_ns * 1e-9)
         m["gips_all"] = m["insts"] / (t_ns * 1e-9) / 1e9
         m["intensity"] = {lv: (m["valu"] / tx[lv] if tx[lv] > 0 else math.inf) for lv in LEVELS}
         m["gbs"] = {lv: tx[lv] * TXN / (t_ns * 1e-9) / 1e9 for lv in LEVELS}
@@ -431,7 +436,7 @@ def render(met: dict, ct: dict, ceil: dict, checks: dict, cal: dict, cmds: list,
     L.append("Instruction counts are wave instructions per dispatch; GIPS over the kernel-trace time.")
     L.append("")
     L.append("MFMA pipe: the fraction of the SIMDs' matrix-pipe clocks (at the nominal clock) the kernel's MFMAs "
-             "occupy, 32 clocks each.")
+             "occupy (SQ_VALU_MFMA_BUSY_CYCLES; where that counter is absent, 32 clocks per MFMA).")
     L.append("")
     L.append("| Kernel | Time (us) | Wave instr | VALU (MFMA) | LDS instr | VMEM rd/wr | GIPS all | GIPS VALU | "
              "MFMA pipe |")
