@@ -186,8 +186,8 @@ def per_config_table(kb, torch, inputs, stream, cache, iters=20, warm_ms=300.0):
 # Datasheet peaks the ceilings are compared with (TFLOP/s; the fp32 vector
 # figure counts packed FMA, which the probe does not use, so its non-packed
 # bound is half of it) and the work per clock per CU of each probe.
-CEIL_PEAK = {"mfma_bf16": 2516.6, "mfma_f32": 157.3, "fma_f32": 157.3 / 2, "exp_f32": None}
-CEIL_PER_CLK_CU = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": None}
+CEIL_PEAK = {"mfma_bf16": 2516.6, "mfma_f32": 157.3, "fma_f32": 157.3 / 2, "exp_f32": None, "mfma_bf16_data": 2516.6}
+CEIL_PER_CLK_CU = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": None, "mfma_bf16_data": 4096}
 CEIL_MEMORY = ("lds_read", "l1_read", "l2_read")  # read-bandwidth probes, bytes per launch
 
 

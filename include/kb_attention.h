@@ -163,8 +163,11 @@ typedef enum {
   KB_CEIL_LDS_READ = 4,  /* ds_read_b128 over a 64 KiB LDS window: 1024 bytes each */
   KB_CEIL_L1_READ = 5,   /* 16-byte-per-lane global loads over a 16 KiB slice per
                             workgroup (vector L1 hits): 1024 bytes each */
-  KB_CEIL_L2_READ = 6    /* the same loads over a 2 MiB region per XCD (L2 hits,
+  KB_CEIL_L2_READ = 6,   /* the same loads over a 2 MiB region per XCD (L2 hits,
                             L1 misses): 1024 bytes each */
+  KB_CEIL_MFMA_BF16_DATA = 7 /* v_mfma_f32_32x32x16_bf16 on random-bit operands
+                                (8 A and 8 B register sets, a new pair for every
+                                product): 32768 flops each */
 } kb_ceiling_kind;
 
 /*

@@ -25,7 +25,8 @@ SIZE_MAX = 2 ** (8 * ctypes.sizeof(ctypes.c_size_t)) - 1
 EXPORTS = ("kb_attention", "kb_attention_workspace_size", "kb_triad", "kb_bench_attention",
            "kb_bench_triad", "kb_bench_stream", "kb_ceiling_work_size", "kb_bench_ceiling", "kb_device_info",
            "kb_status_string", "kb_last_error")
-CEILINGS = {"mfma_bf16": 0, "mfma_f32": 1, "fma_f32": 2, "exp_f32": 3, "lds_read": 4, "l1_read": 5, "l2_read": 6}
+CEILINGS = {"mfma_bf16": 0, "mfma_f32": 1, "fma_f32": 2, "exp_f32": 3, "lds_read": 4, "l1_read": 5, "l2_read": 6,
+            "mfma_bf16_data": 7}
 STREAMS = {"copy": 1, "read": 2, "write": 3}
 STREAM_BYTES = {"triad": 12, "copy": 8, "read": 4, "write": 4}  # per fp32 element
 

@@ -28,6 +28,13 @@
 //                      g reads region g mod 8, the XCD it runs on): larger
 //                      than the vector L1, well inside one XCD's 4 MiB L2,
 //                      the workgroups of an XCD spread over the whole region
+//   KB_CEIL_MFMA_BF16_DATA  v_mfma_f32_32x32x16_bf16 as KB_CEIL_MFMA_BF16,
+//                      but on operands of random bits: 8 A and 8 B register
+//                      sets of random bf16 values (random sign and mantissa,
+//                      magnitudes 2^-4 .. 2^4), a different (A, B) pair for
+//                      each product of 8 consecutive iterations, so the
+//                      matrix core switches data like a real product does
+//                      (the other MFMA kind repeats one constant pair)
 // and each wave records the shader clock counter (s_memtime) and the
 // 100 MHz real-time counter (s_memrealtime) around its loop; their ratio is
 // the clock the wave saw.  Every loaded dword feeds an integer sum written
@@ -48,6 +55,28 @@ constexpr size_t kL1Slice = 16 * 1024;             // per workgroup
 constexpr size_t kL2Region = 2 * 1024 * 1024;      // per XCD
 constexpr int kL2Groups = (int)(kL2Region / (kChains * kChunk));  // 8-chunk groups per region
 constexpr int kXcdRegions = 8;
+
+// Random bf16 bits for the data-driven MFMA probe: a 32-bit integer hash
+// (multiply-xorshift rounds) of the lane, wave, workgroup and slot; random
+// sign and 7-bit mantissa, exponent 123 .. 130.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+__device__ __forceinline__ bf16x8 random_bf16x8(uint32_t key) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t h = mix32(key * 8u + (uint32_t)e);
+    const unsigned short bits = (unsigned short)((h & 0x807Fu) | ((123u + ((h >> 8) & 7u)) << 7));
+    r[e] = __builtin_bit_cast(bf16_t, bits);
+  }
+  return r;
+}
 
 __device__ __forceinline__ void consume(const u32x4 v, uint32_t &s0, uint32_t &s1) {
   s0 += v.x + v.y;
@@ -85,6 +114,35 @@ __global__ __launch_bounds__(kCeilThreads) void ceiling_kernel(int iters, float 
     for (int it = 0; it < iters; ++it)
 #pragma unroll
       for (int c = 0; c < kChains; ++c) acc[c] = mfma32x16_bf16(a, b, acc[c]);
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) r += acc[c][c];
+  } else if constexpr (KIND == KB_CEIL_MFMA_BF16_DATA) {
+    bf16x8 a[kChains], b[kChains];
+    const uint32_t key = (((uint32_t)blockIdx.x * kCeilWaves + (uint32_t)wave) * kWave + (uint32_t)lane) * 16u +
+                         (uint32_t)(seed * 1e3f);
+#pragma unroll
+    for (int i = 0; i < kChains; ++i) {
+      a[i] = random_bf16x8(key + (uint32_t)i);
+      b[i] = random_bf16x8(key + 8u + (uint32_t)i);
+    }
+    f32x16 acc[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
+    // Iteration it uses pair (a[(c + it) % 8], b[(c + 3 it + 1) % 8]) for
+    // chain c: blocks of 8 iterations, then the remainder.
+    auto step = [&](int u) {
+#pragma unroll
+      for (int c = 0; c < kChains; ++c)
+        acc[c] = mfma32x16_bf16(a[(c + u) & 7], b[(c + 3 * u + 1) & 7], acc[c]);
+    };
+    int it = 0;
+    for (; it + 8 <= iters; it += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) step(u);
+    }
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+      if (it + u < iters) step(u);
 #pragma unroll
     for (int c = 0; c < kChains; ++c) r += acc[c][c];
   } else if constexpr (KIND == KB_CEIL_MFMA_F32) {
@@ -143,7 +201,8 @@ __global__ __launch_bounds__(kCeilThreads) void ceiling_kernel(int iters, float 
     }
   }
   const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
-  if constexpr (KIND >= KB_CEIL_LDS_READ) r = __uint_as_float(s0 ^ s1);
+  if constexpr (KIND == KB_CEIL_LDS_READ || KIND == KB_CEIL_L1_READ || KIND == KB_CEIL_L2_READ)
+    r = __uint_as_float(s0 ^ s1);
   const size_t w = (size_t)blockIdx.x * kCeilWaves + wave;
   if (lane == 0) {
     clk[2 * w] = t1 - t0;
@@ -168,7 +227,7 @@ void launch_kind(int cus, int iters, unsigned long long *clk, float *sink, const
 int kb_ceiling_waves(int cus) { return cus * kCeilWaves; }
 
 double kb_ceiling_ops(int kind, int cus, int iters) {
-  const double per_instr = kind == KB_CEIL_MFMA_BF16 ? 2.0 * 32 * 32 * 16
+  const double per_instr = kind == KB_CEIL_MFMA_BF16 || kind == KB_CEIL_MFMA_BF16_DATA ? 2.0 * 32 * 32 * 16
                            : kind == KB_CEIL_MFMA_F32 ? 2.0 * 32 * 32 * 2
                            : kind == KB_CEIL_FMA_F32  ? 2.0 * kWave
                            : kind == KB_CEIL_EXP_F32  ? 1.0 * kWave
@@ -198,6 +257,9 @@ hipError_t kb_launch_ceiling(int kind, int cus, int iters, unsigned long long *c
     case KB_CEIL_LDS_READ: launch_kind<KB_CEIL_LDS_READ>(cus, iters, clk, sink, data, stream); break;
     case KB_CEIL_L1_READ: launch_kind<KB_CEIL_L1_READ>(cus, iters, clk, sink, data, stream); break;
     case KB_CEIL_L2_READ: launch_kind<KB_CEIL_L2_READ>(cus, iters, clk, sink, data, stream); break;
+    case KB_CEIL_MFMA_BF16_DATA:
+      launch_kind<KB_CEIL_MFMA_BF16_DATA>(cus, iters, clk, sink, data, stream);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
