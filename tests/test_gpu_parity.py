@@ -205,6 +205,31 @@ def test_flash_scores_outgrowing_the_reference(d, causal, jump, S):
     compare(o, want, p.dtype, f"growing-keys/S{S}/d{d}/{'c' if causal else 'nc'}/{'jump' if jump else 'steps'}")
 
 
+# A steady tile whose probabilities are each finite but whose sum is not: the
+# scores of every key past the first tile sit about 127.5 log2 units above the
+# reference the first tile sets, so each probability is about 2^127.5 (finite
+# in fp32 and in bf16) and a lane's sum of 32 of them overflows fp32.  The
+# correction has to take the sum again from the corrected probabilities;
+# scaling the infinite sum would give l = inf and a zero output.  All queries
+# are 32 e_0; keys 0..63 have a zero first coordinate, the others `a`
+# (bf16-exact values with 32 a * log2(e) / sqrt(d) = 127.5..127.7).
+_SUM_OVERFLOW_A = {32: 15.625, 64: 22.125, 128: 31.25}
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_flash_steady_tile_sum_overflowing_fp32(d, causal):
+    p = inputs.make_problem(1, 2, 512, d, inputs.BF16, causal=causal, seed=12)
+    x = 32.0 * _SUM_OVERFLOW_A[d] * np.log2(np.e) / np.sqrt(d)
+    assert 127.0 < x < 127.9  # each probability 2^x: finite in bf16, 32 of them overflow fp32
+    p.q[:] = 0.0
+    p.q[:, :, 0] = 32.0
+    p.k[:, :64, 0] = 0.0
+    p.k[:, 64:, 0] = _SUM_OVERFLOW_A[d]
+    o = run(p, "flash").cpu().numpy()
+    compare(o, oracle_full(p), p.dtype, f"sum-overflow/d{d}/{'c' if causal else 'nc'}")
+
+
 # ---------------------------------------------------------------- invariants through the GPU
 
 @pytest.mark.parametrize("variant", VARIANTS)
