@@ -31,6 +31,14 @@ def test_library_exports_every_declared_function():
         assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n
 
 
+def test_ceiling_kinds_match_the_header():
+    """The Python names of the ceiling probes map to the header's
+    kb_ceiling_kind values, every one of them."""
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    kinds = {m.group(1).lower(): int(m.group(2)) for m in re.finditer(r"\bKB_CEIL_([A-Z0-9_]+)\s*=\s*(\d+)", text)}
+    assert kinds == dict(_lib.CEILINGS)
+
+
 def test_status_strings():
     for code in range(6):
         assert kb.kb_status_string(code) and kb.kb_status_string(code) != "unknown status"
