@@ -148,6 +148,17 @@ def test_flash_work_split_over_xcds(causal):
         full_check(p, "flash", f"B{B}H{H}S{S}/d{d}/{'c' if causal else 'nc'}/flash")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_flash_several_units_per_workgroup(causal):
+    """More work units than CUs, so each persistent workgroup runs units of
+    several slices one after another (512 one-tile slices; 160 three-tile
+    slices, whose causal units are a pair and a single middle tile), checked
+    on every element."""
+    for (B, H, S, d) in ((8, 64, 256, 64), (4, 40, 520, 64)):
+        p = inputs.make_problem(B, H, S, d, inputs.BF16, causal=causal, seed=B * H + S)
+        full_check(p, "flash", f"B{B}H{H}S{S}/d{d}/{'c' if causal else 'nc'}/flash")
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_bf16_output(variant):
     """out_dtype bf16 is the fp32 result rounded to nearest even: bit-exact
