@@ -99,15 +99,21 @@ kb_status kb_attention(const kb_attn_cfg *cfg, const void *Q, const void *K, con
 
 /*
  * Bytes of device workspace `variant` needs for `cfg`: 4 * B*H*S*S for
- * KB_NAIVE (the fp32 score / probability matrix), 0 for the others, and
- * (size_t)-1 if cfg is invalid.
+ * KB_NAIVE (the fp32 score / probability matrix that the naive kernel's
+ * first pass writes to DRAM and its softmax and P V passes stream back:
+ * kbench page, "The three GPU kernels", naive), 0 for the others, and
+ * (size_t)-1 if cfg is invalid (the same checks as kb_attention's, made
+ * without touching a device; kb_last_error() says which failed).
  */
 size_t kb_attention_workspace_size(const kb_attn_cfg *cfg, int32_t variant);
 
 /*
  * HBM triad, a[i] = b[i] + s * c[i] for i < n (fp32, 128-bit accesses where
- * alignment allows).  block: threads per workgroup, a multiple of 64 in
+ * alignment allows; the page "TileOPs-Metax benchmarks/hardware", "HBM
+ * Bandwidth": the STREAM triad, two reads and one write per element, is the
+ * calibration kernel).  block: threads per workgroup, a multiple of 64 in
  * [64, 1024].  a, b, c must not overlap.  Enqueued on `stream`.
+ * KB_ERR_INVALID for NULL pointers, n == 0, a bad block or overlap.
  */
 kb_status kb_triad(float *a, const float *b, const float *c, float s, size_t n, int32_t block,
                    void *stream);
@@ -118,12 +124,25 @@ kb_status kb_triad(float *a, const float *b, const float *c, float s, size_t n, 
  * cover exactly the kernels of one call, nothing else).  ms_per_iter (host,
  * length iters) receives each call's GPU time; *ms_total the time from the
  * first to the last event.  Synchronises `stream` before returning.
+ * Protocol: kbench page, "The three GPU kernels", last paragraph (events
+ * around the kernel only, no host-device copies in the window, configurable
+ * warmup, per-launch times for mean / p50 / p99 / min); the warmup also
+ * lets the clocks settle ("TileOPs-Metax benchmarks/hardware",
+ * "Methodology").  Errors: those of kb_attention (before any launch), and
+ * KB_ERR_INVALID for warmup < 0, iters < 1 or NULL result pointers;
+ * KB_ERR_HIP if an event call or launch fails (the stream is synchronised
+ * first).
  */
 kb_status kb_bench_attention(const kb_attn_cfg *cfg, const void *Q, const void *K, const void *V,
                              void *O, int32_t variant, void *stream, int32_t warmup,
                              int32_t iters, float *ms_per_iter, float *ms_total);
 
-/* The same protocol for kb_triad. */
+/*
+ * The same protocol for kb_triad ("TileOPs-Metax benchmarks/hardware",
+ * "Methodology": event timing on the GPU side, warmup iterations before the
+ * timed ones; the caller repeats it per block size and keeps the best).
+ * Errors: those of kb_triad and kb_bench_attention's result checks.
+ */
 kb_status kb_bench_triad(float *a, const float *b, const float *c, float s, size_t n,
                          int32_t block, void *stream, int32_t warmup, int32_t iters,
                          float *ms_per_iter, float *ms_total);
@@ -173,7 +192,9 @@ typedef enum {
 /*
  * Bytes of device work buffer kb_bench_ceiling needs on the current device
  * (per-wave clock counters, one output float per thread and the 16 MiB the
- * cache probes read); 0 if there is no device.
+ * cache probes read); 0 if there is no device.  Same passages as the
+ * probes above: the micro-benchmark log page's compute-peak section records
+ * the clock beside each peak, hence the per-wave clock counters.
  */
 size_t kb_ceiling_work_size(void);
 
@@ -195,7 +216,12 @@ kb_status kb_bench_ceiling(int32_t kind, int32_t iters, void *work, size_t work_
                            int32_t warmup, int32_t reps, float *ms_per_rep, double *ops_per_launch,
                            float *clock_mhz);
 
-/* Properties of the current device, filled by kb_device_info. */
+/*
+ * Properties of the current device, filled by kb_device_info (the kbench
+ * page lists a device_info source beside the kernel launcher, "Repository
+ * layout"; the report needs the chip's name, unit count and clocks to
+ * place each measurement against its ceilings).
+ */
 typedef struct {
   char arch[64];              /* e.g. "gfx950:sramecc+:xnack-" */
   int32_t compute_units;
@@ -205,13 +231,27 @@ typedef struct {
   int64_t global_mem_bytes;
 } kb_device_props;
 
-/* Query the current HIP device.  KB_ERR_NO_DEVICE without a device. */
+/*
+ * Query the current HIP device.  KB_ERR_INVALID if out is NULL;
+ * KB_ERR_NO_DEVICE without a device (the caller then skips its GPU rows
+ * instead of failing: kbench page, "Architecture", the GPU path is
+ * optional and its rows are skipped without a GPU toolkit).
+ */
 kb_status kb_device_info(kb_device_props *out);
 
-/* Static text for a status code (never NULL). */
+/*
+ * Static text for a status code (never NULL; "unknown status" for a value
+ * that is not a kb_status).  Errors are reported, never fatal, so a caller
+ * can skip what the device cannot run (kbench page, "Architecture": GPU
+ * rows are skipped, the run goes on).
+ */
 const char *kb_status_string(int32_t status);
 
-/* Message describing the last failure on the calling thread ("" if none). */
+/*
+ * Message describing the last failure on the calling thread ("" if none;
+ * the text lives in thread-local storage and stays valid until the next
+ * failing call on the same thread).  Same reading as kb_status_string.
+ */
 const char *kb_last_error(void);
 
 #ifdef __cplusplus

@@ -94,6 +94,29 @@ def test_unsupported_dims_and_sizes():
     assert status_of(c) == 1
 
 
+def test_dispatch_limits_of_the_row_per_workgroup_variants():
+    """naive's softmax and fused launch one 256-thread workgroup per query
+    row, so B*H*S must stay below 2^24 rows; naive's slice grid dimension
+    holds at most 65535.  Both are refused before any launch (and before any
+    device query), while flash takes the same shapes."""
+    big_rows = cfg(batch=1, heads=16384, seq=1024, dim=32)  # 2^24 rows, 2^29 elements
+    assert status_of(big_rows, variant="naive") == 2
+    assert status_of(big_rows, variant="fused") == 2
+    assert b"dispatch" in kb.lib().kb_last_error()
+    many_slices = cfg(batch=1, heads=65536, seq=4, dim=32)
+    assert status_of(many_slices, variant="naive") == 2
+    with pytest.raises(kb.KbError):
+        kb.kb_attention_workspace_size(big_rows, "naive")
+    # just under the row limit: accepted by validation (the host has no
+    # device, so a valid call stops at the device check, status 5)
+    import torch
+    if not torch.cuda.is_available():
+        far = tuple(i << 34 for i in range(1, 5))  # 1 GiB tensors must not overlap
+        ok = cfg(batch=1, heads=16383, seq=1024, dim=32)
+        assert status_of(ok, variant="fused", ptrs=far) == 5
+        assert status_of(big_rows, variant="flash", ptrs=far) == 5
+
+
 def test_misaligned_or_overlapping_buffers():
     assert status_of(cfg(), ptrs=(FAKE + 2, FAKE * 2, FAKE * 3, FAKE * 4)) == 1
     # O overlapping Q

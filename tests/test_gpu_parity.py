@@ -3,9 +3,13 @@
 Inputs are the seeded N(0, 1) problems of transformer_attention_micro_amd.inputs
 (bf16 problems rounded once on the host, so both sides see the same values).
 Outputs are pre-filled with NaN so an element the kernels never write fails.
-Small and medium problems are compared on every element; the large ones on
-the tile-edge rows of every head plus 64 seeded rows per head, computed by the
-oracle one row at a time.
+Every variant is compared on every element of the small and medium problems.
+The flash kernel is also compared on every element of the large ones (B2 H32
+S8192 d128 causal, its large-logit variant, and B1 H16 S32768 d128, the last
+split by heads over several tests so each runs in well under a minute on the
+oracle's host threads).  naive and fused, and the extra seeds of the large
+flash problems, are compared on the tile-edge rows of every head plus 64
+seeded rows per head, computed by the oracle one row at a time.
 """
 import numpy as np
 import pytest
@@ -82,11 +86,21 @@ def test_b4h16s2048d64_bf16_causal(variant):
         full_check(p, variant, f"b4h16s2048d64_bf16_causal/seed{seed}/{variant}")
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", ("naive", "fused"))
 @pytest.mark.parametrize("name", ["b2h32s8192d128_bf16_causal", "b2h32s8192d128_bf16_causal_q8"])
 def test_b2h32s8192d128(variant, name):
     p = workload(name)
     sampled_check(p, variant, f"{name}/{variant}")
+
+
+@pytest.mark.parametrize("name", ["b2h32s8192d128_bf16_causal", "b2h32s8192d128_bf16_causal_q8"])
+def test_b2h32s8192d128_flash_every_row(name):
+    """The measured kernel and its large-logit variant, all 524,288 output
+    rows against the oracle (on all host threads)."""
+    p = workload(name)
+    o = run(p, "flash").cpu().numpy()
+    want = oracle.sdpa(p.q, p.k, p.v, causal=p.causal)
+    compare(o, want, p.dtype, f"{name}/flash/every-row")
 
 
 @pytest.mark.parametrize("seed", [1, 2])
@@ -101,7 +115,30 @@ def test_b2h32s8192d128_flash_more_seeds(name, seed):
     compare(o[rows], want, p.dtype, f"{name}/seed{seed}/flash")
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+_C5_PARTS = 8
+_flash_outputs = {}
+
+
+@pytest.mark.parametrize("part", range(_C5_PARTS))
+def test_b1h16s32768d128_flash_every_row(part):
+    """The long non-causal workload, every output row: the flash output is
+    computed once, and each part compares 2 of the 16 heads (65,536 rows)
+    against the oracle."""
+    name = "b1h16s32768d128_bf16"
+    p = workload(name)
+    if name not in _flash_outputs:
+        _flash_outputs[name] = run(p, "flash").cpu().numpy()
+    o = _flash_outputs[name]
+    per = p.BH // _C5_PARTS
+    h0, h1 = part * per, (part + 1) * per
+    rows = np.arange(h0 * p.S, h1 * p.S, dtype=np.int64)
+    want = oracle.sdpa(p.q, p.k, p.v, causal=p.causal, rows=rows)
+    compare(o[h0:h1].reshape(-1, p.d), want, p.dtype, f"{name}/flash/heads{h0}-{h1 - 1}")
+    if part == _C5_PARTS - 1:
+        _flash_outputs.pop(name, None)
+
+
+@pytest.mark.parametrize("variant", ("naive", "fused"))
 def test_b1h16s32768d128_bf16(variant):
     p = workload("b1h16s32768d128_bf16")
     try:
@@ -401,3 +438,50 @@ def test_bandwidth_kernels_move_the_right_bytes():
     kb.triad(a, b, c, 1.5)
     torch.cuda.synchronize()
     assert torch.allclose(a, b + 1.5 * c, rtol=0, atol=1e-6)
+
+
+def test_triad_values_at_the_calibration_size_and_on_tails():
+    """The triad at the calibration's 2 GiB working set, and on lengths and
+    offsets that take its scalar path: an aligned length with a 3-element
+    tail (vector body plus scalar tail) and buffers one element off 16-byte
+    alignment (scalar throughout).  s = 2 makes s * c exact, so the fused
+    multiply-add equals b + 2 c bit for bit."""
+    torch = torch_cuda()
+    n = 2048 * 1024 * 1024 // 12
+    n -= n % 4
+    b = torch.rand(n, device="cuda")
+    c = torch.rand(n, device="cuda")
+    a = torch.full((n,), float("nan"), device="cuda")
+    for block in (64, 1024):
+        a.fill_(float("nan"))
+        kb.triad(a, b, c, 2.0, block=block)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b + 2.0 * c), f"2 GiB, block {block}"
+    del a, b, c
+    torch.cuda.empty_cache()
+    m = (1 << 20) + 7
+    b = torch.rand(m + 1, device="cuda")
+    c = torch.rand(m + 1, device="cuda")
+    for off, label in ((0, "vector body + 3-element tail"), (1, "misaligned, scalar")):
+        a = torch.full((m + 1,), float("nan"), device="cuda")
+        kb.triad(a[off:off + m], b[off:off + m], c[off:off + m], 2.0)
+        torch.cuda.synchronize()
+        want = b[off:off + m] + 2.0 * c[off:off + m]
+        assert torch.equal(a[off:off + m], want), label
+        untouched = a[m:] if off == 0 else a[:1]
+        assert torch.isnan(untouched).all(), f"{label}: wrote outside the range"
+
+
+def test_binding_rejects_host_output_and_workspace():
+    """attention() refuses an output or workspace tensor that is not on Q's
+    GPU before anything is launched (its address would be a host pointer in
+    the kernels)."""
+    torch = torch_cuda()
+    p = inputs.make_problem(1, 2, 64, 32, inputs.F32, seed=3)
+    q, k, v = to_device(p)
+    with pytest.raises(ValueError):
+        kb.attention(q, k, v, torch.empty(q.shape, dtype=torch.float32), variant="flash")
+    with pytest.raises(ValueError):
+        kb.attention(q, k, v, variant="naive", workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        kb.attention(q, k.cpu(), v, variant="flash")

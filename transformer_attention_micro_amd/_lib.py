@@ -224,11 +224,17 @@ def attention(q, k, v, out=None, *, causal: bool = False, variant="flash", scale
             raise ValueError("Q, K, V must be contiguous CUDA tensors")
     if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
         raise ValueError("Q, K, V must share shape and dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("Q, K, V must be on one device")
     B, H, S, d = _shape(q, heads)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     elif out.dtype not in (torch.float32, torch.bfloat16) or out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 or bfloat16 tensor shaped like Q")
+    # The kernels write O (and naive's workspace) through raw device
+    # pointers: a host tensor's address there would be a GPU memory fault.
+    if not out.is_cuda or out.device != q.device:
+        raise ValueError("out must be a CUDA tensor on Q's device")
     cfg = make_cfg(B, H, S, d, causal, _dtype_code(q), scale,
                    out_dtype=KB_BF16 if out.dtype == torch.bfloat16 else KB_F32)
     vcode = _variant(variant)
@@ -236,6 +242,8 @@ def attention(q, k, v, out=None, *, causal: bool = False, variant="flash", scale
         need = kb_attention_workspace_size(cfg, vcode)
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA tensor on Q's device")
         cfg.workspace = workspace.data_ptr()
         cfg.workspace_bytes = workspace.numel() * workspace.element_size()
     kb_attention(cfg, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), vcode,

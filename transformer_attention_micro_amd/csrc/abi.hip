@@ -115,6 +115,22 @@ kb_status validate(const kb_attn_cfg *cfg, int32_t variant, kb_problem *p) {
     set_err("naive score matrix exceeds 2^40 elements");
     return KB_ERR_UNSUPPORTED;
   }
+  // Dispatch limits, checked here so that no kernel of a multi-pass variant
+  // is enqueued before a later one fails to launch: a dispatch holds fewer
+  // than 2^32 work-items per grid dimension, and the y / z grid dimensions
+  // (naive: one per slice) at most 65535 workgroups.  The naive softmax and
+  // the fused kernel launch one 256-thread workgroup per query row.
+  if (variant == KB_NAIVE || variant == KB_FUSED) {
+    if (bh * cfg->seq * 256LL > 0xffffffffLL) {
+      set_err("%lld query rows exceed the dispatch limit of the %s variant (2^24 rows)", bh * cfg->seq,
+              variant == KB_NAIVE ? "naive" : "fused");
+      return KB_ERR_UNSUPPORTED;
+    }
+    if (variant == KB_NAIVE && bh > 65535) {
+      set_err("naive launches one grid row per slice: %lld slices exceed 65535", bh);
+      return KB_ERR_UNSUPPORTED;
+    }
+  }
   p->bh = (int)bh;
   p->S = cfg->seq;
   p->D = cfg->dim;

@@ -285,16 +285,22 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
       return (uint32_t)__builtin_amdgcn_readfirstlane(t < ntiles ? (uint32_t)t * BC * 2u * D : head_bytes);
     };
     // Load instruction i (0 <= i < CHW) of tile `t` of K (is_v false) or V.
+    // The statements write m0 (the LDS destination of the load), so it is in
+    // their clobber list; the compiler then knows m0 changed (it warns that a
+    // reserved register is not preserved, which is what is meant here).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
     auto dma = [&](bool is_v, int i, lds_bf16 *dst, uint32_t toff) KB_INLINE {
       if (w + NW * i >= NI) return;
       const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + (w + NW * i) * 512));
       if (is_v)
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :: "s"(m0), "v"(voff[i]), "s"(rv), "s"(toff) : "memory");
+                     :: "s"(m0), "v"(voff[i]), "s"(rv), "s"(toff) : "memory", "m0");
       else
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :: "s"(m0), "v"(koff[i]), "s"(rk), "s"(toff) : "memory");
+                     :: "s"(m0), "v"(koff[i]), "s"(rk), "s"(toff) : "memory", "m0");
     };
+#pragma clang diagnostic pop
     auto load_tile = [&](bool is_v, lds_bf16 *dst, int t) KB_INLINE {
       const uint32_t toff = tile_off(t);
   #pragma unroll
@@ -436,27 +442,28 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
       m_run = m_new;
       return grow;
     };
-    // Softmax, second part, for key half sb: exponentials, bf16 probabilities
-    // (the P operand of P V) and their fp32 sum.  The sum uses plain adds: the
-    // packed dot-product instruction would run on the matrix pipeline and
-    // delay the MFMAs.
-    auto probs = [&](int sb, float &ls) KB_INLINE {
+    // Softmax, second part, for key half sb: exponentials and the bf16
+    // probabilities (the P operand of P V).
+    auto probs = [&](int sb) KB_INLINE {
       const float nm = -m_run;
   #pragma unroll
       for (int v = 0; v < 16; ++v) sc[sb][v] = exp2_fast(fmaf(sc[sb][v], sl2e, nm));
-      float s0 = 0.f, s1 = 0.f;
-  #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        s0 += sc[sb][v];
-        s1 += sc[sb][v + 1];
-      }
-      ls += s0 + s1;
   #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const int cc = 2 * sb + c2;
   #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2) pb[cc][s2] = (bf16_t)sc[sb][8 * c2 + s2];
       }
+    };
+    // The lane's share of the row sum l for the current tile: the fp32 sum of
+    // its 32 bf16 probabilities, the very weights P V multiplies (so O is
+    // divided by exactly the total of the weights it summed), by the row-sum
+    // MFMAs described at sum_a.  Every tile takes l this way.
+    auto pb_sum = [&]() KB_INLINE {
+      f32x4 s4 = f32x4{};
+  #pragma unroll
+      for (int cc = 0; cc < 4; ++cc) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sum_a, pb[cc], s4, 0, 0, 0);
+      return s4[0];
     };
 
     // Steady-state step: O += P(t-1) V(t-1), the softmax of t and S^T(t+1) as
@@ -615,10 +622,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
         pb[cc] = __builtin_bit_cast(bf16x8, wds);
       }
       // The tile's sum from the corrected probabilities (each now below 1).
-      f32x4 s4 = f32x4{};
-  #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sum_a, pb[cc], s4, 0, 0, 0);
-      ls = s4[0];
+      ls = pb_sum();
       m_run += (float)k;
       l_run *= alpha;
   #pragma unroll
@@ -683,10 +687,9 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
       if (t < tw) {
         mask(t);
         grow = row_max(alpha, kRescaleLog2);
-        float ls = 0.f;
-        probs(0, ls);
-        probs(1, ls);
-        l_run += ls;
+        probs(0);
+        probs(1);
+        l_run += pb_sum();
       }
       if (t + 1 < tw) qk(kst((st + 1) & 3));
       rescale(grow, alpha);
