@@ -4,42 +4,53 @@
 
 One step is one attention forward pass (kb_attention, variant flash) over the
 workload B=2, H=32, S=8192, d=128, bf16 inputs, causal mask, fp32 output,
-with Q, K, V already resident in HBM.  The default warmup (200 launches,
-~0.2 s) outlasts the clock transient of an MI355X coming out of idle (a few
-fast launches, a dip of up to ~30 %, then ~0.1 s of recovery), so the timed
-steps measure sustained throughput.  The K timed steps are bracketed by
-torch.cuda.synchronize() on both sides; inside, kb_bench_attention records a
-hipEvent between consecutive launches on the launch stream, which gives the
-per-launch kernel time used for the roofline fraction.
+with Q, K, V already resident in HBM.  W untimed launches, then the K timed
+steps, bracketed by torch.cuda.synchronize() on both sides; inside,
+kb_bench_attention records a hipEvent between consecutive launches on the
+launch stream, which gives the per-launch kernel time used for the roofline
+fraction.  The default warmup (200 launches, ~0.2 s) outlasts the clock
+transient of an MI355X coming out of idle (a few fast launches, a dip of up
+to ~30 %, then ~0.1 s of recovery); a short warmup leaves the timed steps
+inside it, and the line says so (`protocol` and `per_config` below are
+always measured warm).
 
 The JSON line also carries:
   roofline      achieved TFLOP/s per launch vs the MI355X dense bf16 MFMA
                 peak (2516.6 TFLOP/s), and HBM bytes per launch from the
                 rocprofv3 FETCH_SIZE / WRITE_SIZE summary committed under
                 profiles/ (null if the kernel changed since it was taken);
+  protocol      the headline launch under the HBM page's timing protocol
+                (100 warmup launches, then 200 launches x 5 runs; best and
+                median of the runs' mean times);
+  per_config    every configured workload (and the S=8192 one without the
+                mask) x every variant (flash, naive, fused): min / p50 / p99
+                / mean kernel time, TFLOP/s and the fraction of the dtype's
+                MFMA peak, algorithmic GB/s and the fraction of 8 TB/s, the
+                shader clock and socket power sampled during the timed
+                launches, and the max-abs / relative-L2 error against the
+                oracle (filled in by the CPU leg; every row for S <= 2048,
+                the tile-edge rows plus 64 seeded rows per head above);
+                a variant that cannot run a workload says why;
+  hbm           the triad calibration and the copy / read-only / write-only
+                reference kernels at a 2 GiB working set under the same
+                protocol, best over a block-size sweep;
+  ceilings      sustained compute and on-chip bandwidth ceilings
+                (kb_bench_ceiling) with the shader clock each probe ran at;
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded,
-                seeded sample of the same workload's query rows (also used
-                to check the GPU output on those rows); small_configs: the
-                oracle on every row of each workload with S <= 2048, on all
-                threads and on one, beside the GPU's time and its error;
-  triad         the HBM triad calibration (best of a block-size sweep);
-  hbm_reference copy, read-only and write-only kernels at the same 2 GiB
-                working set (best of the same sweep);
-  variants      naive and fused on the same workload (a few timed calls);
-  per_config    flash on every configured workload (the metric is quoted per
-                (B, H, S, d), causal or not), each warmed up for ~0.3 s:
-                mean hipEvent time per launch, TFLOP/s and the fraction of
-                the dtype's MFMA peak;
-  ceilings      sustained compute ceilings (kb_bench_ceiling: bf16 and fp32
-                MFMA, fp32 FMA, exp) with the shader clock the probe ran at,
-                the compute analogue of the triad.
+                seeded sample of the headline workload's query rows (also
+                used to check the GPU output on those rows), with the host's
+                physical core count and SMT state; small_configs: the oracle
+                on every row of each workload with S <= 2048, on all threads
+                and on one, beside the GPU's time and its error.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -51,6 +62,7 @@ if ROOT not in sys.path:
 METRIC = "SDPA forward TFLOP/s + % of MFMA peak per (B,H,S,d), causal/non-causal"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
 HBM_PEAK_GBS = 8000.0
+HEADLINE = "b2h32s8192d128_bf16_causal"
 
 
 def parse():
@@ -58,12 +70,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="b2h32s8192d128_bf16_causal")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--no-extras", action="store_true", help="skip triad and the naive/fused variants")
+    ap.add_argument("--no-extras", action="store_true", help="skip the HBM calibration and the protocol block")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the flash table over every configured workload")
+                    help="skip the table over every configured workload and variant")
+    ap.add_argument("--flash-only", action="store_true", help="the per-config table for the flash variant only")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the compute-ceiling probes")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB three times "
@@ -82,6 +95,207 @@ def device_tensors(p, torch):
         else:
             out.append(torch.from_numpy(a).cuda())
     return out
+
+
+# ---------------------------------------------------------------- clocks
+
+class ClockSampler:
+    """Samples the GPU's shader clock (mean over the XCDs) and socket power
+    through amdsmi in a background thread while a measurement runs.  Without
+    amdsmi access every field is None and `error` says why."""
+
+    def __init__(self, period_s: float = 0.01):
+        self.period = period_s
+        self.error = None
+        self.handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self.read()
+        except Exception as e:  # no driver access: report, do not fail the bench
+            self.error = f"{type(e).__name__}: {e}"
+            self.handle = None
+
+    def read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = m.get("current_gfxclks")
+        vals = [c for c in clks if isinstance(c, (int, float)) and 0 < c < 10000] if isinstance(clks, list) else []
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [m["current_gfxclk"]]
+        pw = m.get("current_socket_power")
+        return (float(np.mean(vals)) if vals else None, float(pw) if isinstance(pw, (int, float)) else None)
+
+    def __enter__(self):
+        self.samples = []
+        self._stop = threading.Event()
+        if self.handle is not None:
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+        return self
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self.read())
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.handle is not None:
+            self._t.join()
+        return False
+
+    def summary(self):
+        clk = [c for c, _ in self.samples if c is not None]
+        pw = [p for _, p in self.samples if p is not None]
+        if not clk:
+            return {"gfx_mhz_mean": None, "error": self.error or "no samples"}
+        return {"gfx_mhz_mean": round(float(np.mean(clk)), 0), "gfx_mhz_min": round(min(clk), 0),
+                "gfx_mhz_max": round(max(clk), 0), "gfx_mhz_first": round(clk[0], 0),
+                "gfx_mhz_last": round(clk[-1], 0),
+                "socket_power_w_mean": round(float(np.mean(pw)), 0) if pw else None, "samples": len(clk)}
+
+
+# ---------------------------------------------------------------- timing helpers
+
+def time_stats(per):
+    a = np.asarray(per, dtype=np.float64)
+    return {"n": int(a.size), "min": round(float(a.min()), 4), "p50": round(float(np.median(a)), 4),
+            "p99": round(float(np.percentile(a, 99)), 4), "mean": round(float(a.mean()), 4)}
+
+
+def sample_rows(S: int, BH: int, seed: int = 0, per_head: int = 64):
+    """Flat row ids bh * S + i: the tile-edge rows of every head plus seeded
+    rows (the rows the oracle checks when it cannot afford all of them)."""
+    edges = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 511, 512, S // 2, S - 2, S - 1}
+    rng = np.random.default_rng(seed)
+    rows = []
+    for bh in range(BH):
+        r = {e for e in edges if 0 <= e < S}
+        r |= set(rng.integers(0, S, size=per_head).tolist())
+        rows.extend(bh * S + i for i in sorted(r))
+    return np.array(rows, dtype=np.int64)
+
+
+def algorithmic_bytes(kb, p, variant):
+    """Compulsory bytes (Q, K, V read once, fp32 O written once) plus, for
+    naive, the fp32 score matrix written, read and rewritten by the softmax
+    and read by P V (16 bytes per score)."""
+    comp = kb.attention_bytes(p.B, p.H, p.S, p.d, 2 if p.dtype == "bf16" else 4)
+    return comp + (16 * p.BH * p.S * p.S if variant == "naive" else 0)
+
+
+def per_config_table(kb, torch, inputs, stream, cache, sampler, checks, variants=("flash", "naive", "fused"),
+                     flash_iters=100, warm_ms=300.0, budget_ms=600.0):
+    """Every configured workload x variant x mask.  flash first (each row
+    warmed for >= warm_ms, so none sits in a clock transient; before the
+    HBM-bound variants heat the GPU), then naive and fused (one warm launch,
+    then as many timed launches as fit in ~budget_ms, at least 3).  Each
+    row keeps the output rows the oracle will check in `checks`."""
+    rows = []
+    free = torch.cuda.mem_get_info()[0]
+    for vpass in (("flash",), tuple(v for v in variants if v != "flash")):
+        for name in inputs.WORKLOADS:
+            if not vpass:
+                break
+            p = cache[name] if name in cache else inputs.workload(name)
+            q, k, v = device_tensors(p, torch)
+            o = torch.empty((p.BH, p.S, p.d), dtype=torch.float32, device="cuda")
+            dt = kb.KB_BF16 if p.dtype == inputs.BF16 else kb.KB_F32
+            rid = None if p.S <= 2048 else sample_rows(p.S, p.BH)
+            for causal in ([True, False] if name == HEADLINE else [p.causal]):
+                for variant in vpass:
+                    row = {"workload": name, "B": p.B, "H": p.H, "S": p.S, "d": p.d, "causal": causal,
+                           "dtype": p.dtype, "variant": variant}
+                    ws = None
+                    try:
+                        cfg = kb.make_cfg(p.B, p.H, p.S, p.d, causal, dt)
+                        if variant == "naive":
+                            need = kb.kb_attention_workspace_size(cfg, "naive")
+                            if need > free - (8 << 30):
+                                raise kb.KbError(3, "workspace", f"{need} bytes do not fit in device memory")
+                            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+                            cfg = kb.make_cfg(p.B, p.H, p.S, p.d, causal, dt, 0.0, ws.data_ptr(), need)
+                        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
+                        first, _ = kb.kb_bench_attention(cfg, *ptrs, variant, stream, 0, 1)
+                        t1 = max(first[0], 1e-3)
+                        if variant == "flash":
+                            warm, iters = max(3, int(np.ceil(warm_ms / t1))), flash_iters
+                        else:
+                            warm, iters = 1, int(min(100, max(3, budget_ms / t1)))
+                        kb.kb_bench_attention(cfg, *ptrs, variant, stream, warm, 1)
+                        with sampler:
+                            per, _ = kb.kb_bench_attention(cfg, *ptrs, variant, stream, 0, iters)
+                        st = time_stats(per)
+                        fl = kb.attention_flops(p.B, p.H, p.S, p.d, causal)
+                        nb = algorithmic_bytes(kb, p, variant)
+                        tf = fl / (st["p50"] * 1e-3) / 1e12
+                        gbs = nb / (st["p50"] * 1e-3) / 1e9
+                        row.update({"kernel_ms": st, "tflops": round(tf, 2),
+                                    "frac_of_peak": round(tf / PEAK_TFLOPS[p.dtype], 4),
+                                    "tflops_at_mean": round(fl / (st["mean"] * 1e-3) / 1e12, 2),
+                                    "algorithmic_bytes": nb, "gbs": round(gbs, 1),
+                                    "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4), "clock": sampler.summary(),
+                                    "max_abs_err": None, "rel_l2_err": None})
+                        torch.cuda.synchronize()
+                        got = o.cpu().numpy().reshape(p.BH * p.S, p.d)
+                        checks.append((row, name, causal, rid, got if rid is None else got[rid].copy()))
+                    except kb.KbError as e:
+                        row["status"] = str(e)
+                    rows.append(row)
+                    print(f"[per_config] {name} {'c' if causal else 'nc'} {variant}: "
+                          f"{row.get('kernel_ms', {}).get('p50', row.get('status'))}", file=sys.stderr,
+                          flush=True)
+                    del ws
+                    torch.cuda.empty_cache()
+            del q, k, v, o
+            torch.cuda.empty_cache()
+    return rows
+
+
+def headline_protocol(kb, cfg, ptrs, stream, flops, peak, warmup=100, runs=5, iters=200):
+    """The HBM page's timing protocol ("Methodology") applied to the headline
+    launch: `warmup` launches, then `runs` runs of `iters` timed launches;
+    the best and the median of the runs' mean times."""
+    means = []
+    for r in range(runs):
+        per, _ = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, warmup if r == 0 else 0, iters)
+        means.append(float(np.mean(per)))
+    best, med = min(means), float(np.median(means))
+    return {"warmup": warmup, "runs": runs, "iters": iters, "run_mean_ms": [round(m, 4) for m in means],
+            "best_ms": round(best, 4), "median_ms": round(med, 4),
+            "tflops_best": round(flops / (best * 1e-3) / 1e12, 2), "tflops_median": round(flops / (med * 1e-3) / 1e12, 2),
+            "frac_best": round(flops / (best * 1e-3) / 1e12 / peak, 4),
+            "frac_median": round(flops / (med * 1e-3) / 1e12 / peak, 4)}
+
+
+# ---------------------------------------------------------------- CPU leg (the oracle)
+
+def host_cpu():
+    """Physical cores, SMT threads per core and the model name (lscpu), and
+    the CPUs this process may use."""
+    info = {"affinity_cpus": len(os.sched_getaffinity(0))}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        kv = {}
+        for line in out.splitlines():
+            if ":" in line:
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+        sockets = int(kv.get("Socket(s)", "0") or 0)
+        cps = int(kv.get("Core(s) per socket", "0") or 0)
+        tpc = int(kv.get("Thread(s) per core", "0") or 0)
+        info.update({"physical_cores": sockets * cps or None, "sockets": sockets or None,
+                     "smt_threads_per_core": tpc or None, "smt_on": (tpc > 1) if tpc else None,
+                     "logical_cpus": int(kv.get("CPU(s)", "0") or 0) or None, "model": kv.get("Model name")})
+    except Exception as e:
+        info["lscpu_error"] = f"{type(e).__name__}: {e}"
+    return info
 
 
 def cpu_baseline(p, o_gpu, budget_s, seed=1234):
@@ -111,15 +325,37 @@ def cpu_baseline(p, o_gpu, budget_s, seed=1234):
         if t_used > 0.5 * budget_s and chunk < 4096:
             chunk *= 2
     n = int(sum(len(r) for r in rows_done))
+    cpu = host_cpu()
     return {
         "value": flops / t_used / 1e12,
         "unit": "TFLOP/s",
         "cores": nthreads,
         "kind": "oracle",
         "sample": f"{n} distinct seeded query rows (of {p.BH * p.S}) of the same workload, fp64, "
-                  f"{t_used:.1f} s; throughput scaled by the rows' algorithmic FLOPs",
+                  f"{t_used:.1f} s on {nthreads} threads ({cpu.get('physical_cores')} physical cores, "
+                  f"{cpu.get('smt_threads_per_core')} threads per core); throughput scaled by the rows' "
+                  f"algorithmic FLOPs",
+        "host": cpu,
         "max_abs_err_vs_gpu_on_sample": max(errs),
     }
+
+
+def fill_errors(checks, inputs, cache):
+    """The oracle on the rows each per-config row kept; one oracle evaluation
+    per (workload, mask), shared by the variants."""
+    import oracle
+    refs = {}
+    for row, name, causal, rid, got in checks:
+        key = (name, causal)
+        if key not in refs:
+            p = cache[name] if name in cache else inputs.workload(name)
+            want = oracle.sdpa(p.q, p.k, p.v, causal=causal, rows=rid)
+            refs[key] = want.reshape(-1, p.d)
+        want = refs[key]
+        g = np.asarray(got, dtype=np.float64)
+        row["max_abs_err"] = float(np.max(np.abs(g - want)))
+        row["rel_l2_err"] = float(np.linalg.norm(g - want) / np.linalg.norm(want))
+        row["rows_checked"] = "all" if rid is None else int(len(rid))
 
 
 def cpu_small_configs(kb, torch, inputs, stream):
@@ -156,32 +392,7 @@ def cpu_small_configs(kb, torch, inputs, stream):
     return out
 
 
-def per_config_table(kb, torch, inputs, stream, cache, iters=20, warm_ms=300.0):
-    """Flash on every configured workload (seeded inputs per the recipe; the
-    S=8192 workload also without the mask), each warmed up for at least
-    warm_ms so the row is not measured inside a clock transient."""
-    rows = []
-    for name in inputs.WORKLOADS:
-        p = cache[name] if name in cache else inputs.workload(name)
-        q, k, v = device_tensors(p, torch)
-        o = torch.empty((p.BH, p.S, p.d), dtype=torch.float32, device="cuda")
-        dt = kb.KB_BF16 if p.dtype == inputs.BF16 else kb.KB_F32
-        for causal in ([True, False] if name == "b2h32s8192d128_bf16_causal" else [p.causal]):
-            cfg = kb.make_cfg(p.B, p.H, p.S, p.d, causal, dt)
-            ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
-            first, _ = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, 0, 1)
-            warm = max(3, int(np.ceil(warm_ms / max(first[0], 1e-3))))
-            per, _ = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, warm, iters)
-            ms = float(np.mean(per))
-            fl = kb.attention_flops(p.B, p.H, p.S, p.d, causal)
-            tf = fl / (ms * 1e-3) / 1e12
-            rows.append({"workload": name, "B": p.B, "H": p.H, "S": p.S, "d": p.d, "causal": causal,
-                         "dtype": p.dtype, "kernel_ms_mean": round(ms, 4), "tflops": round(tf, 2),
-                         "frac_of_peak": round(tf / PEAK_TFLOPS[p.dtype], 4)})
-        del q, k, v, o
-        torch.cuda.empty_cache()
-    return rows
-
+# ---------------------------------------------------------------- ceilings
 
 # Datasheet peaks the ceilings are compared with (TFLOP/s; the fp32 vector
 # figure counts packed FMA, which the probe does not use, so its non-packed
@@ -238,25 +449,6 @@ def measured_traffic(workload):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def triad_calibration(kb, torch, stream):
-    n = 2048 * 1024 * 1024 // 12  # 2048 MiB working set over a, b, c
-    n -= n % 4
-    a = torch.empty(n, dtype=torch.float32, device="cuda")
-    b = torch.rand(n, dtype=torch.float32, device="cuda")
-    c = torch.rand(n, dtype=torch.float32, device="cuda")
-    best = None
-    for block in (64, 128, 256, 512, 1024):
-        per, _ = kb.kb_bench_triad(a.data_ptr(), b.data_ptr(), c.data_ptr(), 1.5, n, block, stream, 20, 50)
-        ms = float(np.median(per))
-        gbs = 12.0 * n / (ms * 1e-3) / 1e9
-        if best is None or gbs > best["gbs"]:
-            best = {"gbs": gbs, "block": block, "median_ms": ms}
-    del a, b, c
-    torch.cuda.empty_cache()
-    return {"best_gbs": round(best["gbs"], 1), "block": best["block"], "bytes": 12 * n,
-            "calibration_vs_8000": round(best["gbs"] / HBM_PEAK_GBS, 4)}
-
-
 def main():
     args = parse()
     if args.gpus != 1:
@@ -281,14 +473,16 @@ def main():
     stream = int(torch.cuda.current_stream().cuda_stream)
     flops = kb.attention_flops(p.B, p.H, p.S, p.d, p.causal)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
+    sampler = ClockSampler()
 
     for _ in range(args.warmup):
         kb.kb_attention(cfg, *ptrs, "flash", stream)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    per, total_ms = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, 0, args.steps)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with sampler:
+        t0 = time.perf_counter()
+        per, total_ms = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, 0, args.steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     kern_ms = float(np.mean(per))
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -317,13 +511,22 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_min": round(float(np.min(per)), 4),
                      "kernel_ms_p50": round(float(np.median(per)), 4),
-                     "kernel_ms_p99": round(float(np.percentile(per, 99)), 4)},
+                     "kernel_ms_p99": round(float(np.percentile(per, 99)), 4),
+                     "clock": sampler.summary()},
     }
+    if args.warmup < 100:
+        result["roofline"]["note"] = (f"{args.warmup} warmup launches leave the timed ones inside the clock "
+                                      f"transient of a GPU coming out of idle; 'protocol' and 'per_config' "
+                                      f"are measured warm")
 
-    # Right after the main measurement, before the HBM-bound legs heat the
-    # GPU (a heat-soaked MI355X runs the same flash launch up to ~17% slower).
+    if not args.no_extras:
+        result["protocol"] = headline_protocol(kb, cfg, ptrs, stream, flops, peak)
+
+    checks = []
+    cache = {args.workload: p}
     if not args.no_configs:
-        result["per_config"] = per_config_table(kb, torch, inputs, stream, {args.workload: p})
+        variants = ("flash",) if args.flash_only else ("flash", "naive", "fused")
+        result["per_config"] = per_config_table(kb, torch, inputs, stream, cache, sampler, checks, variants)
 
     if args.copy_mib > 0:
         n = args.copy_mib * (1 << 20) // 4
@@ -336,29 +539,12 @@ def main():
         del src, dst
 
     if not args.no_extras:
-        extras = {}
-        ws = torch.empty(kb.kb_attention_workspace_size(cfg, "naive"), dtype=torch.uint8, device="cuda")
-        ncfg = kb.make_cfg(p.B, p.H, p.S, p.d, p.causal, dt, 0.0, ws.data_ptr(), ws.numel())
-        for name, c in (("naive", ncfg), ("fused", cfg)):
-            try:
-                pv, _ = kb.kb_bench_attention(c, *ptrs, name, stream, 1, 3)
-                ms = float(np.median(pv))
-                extras[name] = {"ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
-                if name == "naive":
-                    nbytes = 16 * p.BH * p.S * p.S + kb.attention_bytes(p.B, p.H, p.S, p.d, 2 if dt else 4)
-                    extras[name]["hbm_gbs_algorithmic"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
-            except kb.KbError as e:
-                extras[name] = {"error": str(e)}
-        del ws
-        torch.cuda.empty_cache()
-        result["variants"] = extras
-        result["triad"] = triad_calibration(kb, torch, stream)
-        from transformer_attention_micro_amd.hbm import best_gbs
-        ref = {}
-        for kind in ("copy", "read", "write"):
-            gbs, block = best_gbs(kb, torch, kind, 2048, (64, 128, 256, 512, 1024), stream, 10, 30)
-            ref[kind] = {"gbs": round(gbs, 1), "block": block, "frac_of_8000": round(gbs / HBM_PEAK_GBS, 4)}
-        result["hbm_reference"] = ref
+        from transformer_attention_micro_amd import hbm
+        cal = hbm.calibrate(kb, torch, stream)
+        result["hbm"] = {"calibration_vs_8000": cal["calibration"],
+                         "protocol": cal["protocol"], "working_set_mib": cal["working_set_mib"],
+                         **{kind: {x: cal[kind][x] for x in ("best_gbs", "median_gbs", "best_block")}
+                            for kind in ("triad", "copy", "read", "write")}}
 
     if not args.no_ceilings:
         result["ceilings"] = ceilings(kb, torch, stream)
@@ -369,6 +555,8 @@ def main():
         o_host = o.cpu().numpy().reshape(p.BH * p.S, p.d).astype(np.float64)
         result["cpu_baseline"] = cpu_baseline(p, o_host, args.cpu_seconds)
         result["cpu_baseline"]["small_configs"] = cpu_small_configs(kb, torch, inputs, stream)
+        if checks:
+            fill_errors(checks, inputs, cache)
 
     print(json.dumps(result), flush=True)
     return 0
