@@ -98,6 +98,27 @@ kb_status kb_attention(const kb_attn_cfg *cfg, const void *Q, const void *K, con
                        void *O, int32_t variant, void *stream);
 
 /*
+ * kb_attention(cfg, Q, K, V, O, KB_NAIVE, stream) without a caller-provided
+ * workspace and without allocating: for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The naive variant's fp32 score matrix goes to a
+ * static device array of KB_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on each GPU it runs on until the process ends (its device address
+ * is looked up once per device, on the first call made with that device
+ * current).  cfg->workspace and cfg->workspace_bytes are ignored.  Limit:
+ * 4 * batch * heads * seq * seq <= KB_NOALLOC_SCRATCH_BYTES (e.g. 16 heads
+ * at seq 1024), else KB_ERR_WORKSPACE before any launch.  Every call on one
+ * GPU uses the same array, so calls that overlap on one GPU (other streams
+ * or host threads) race and must be serialised by the caller.  Nothing in
+ * the array needs to start at zero: the first pass writes every score the
+ * later passes read.  Other errors as kb_attention; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ */
+#define KB_NOALLOC_SCRATCH_BYTES (64u << 20)
+kb_status kb_attention_naive_noalloc(const kb_attn_cfg *cfg, const void *Q, const void *K, const void *V,
+                                     void *O, void *stream);
+
+/*
  * Bytes of device workspace `variant` needs for `cfg`: 4 * B*H*S*S for
  * KB_NAIVE (the fp32 score / probability matrix that the naive kernel's
  * first pass writes to DRAM and its softmax and P V passes stream back:

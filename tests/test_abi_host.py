@@ -117,6 +117,23 @@ def test_dispatch_limits_of_the_row_per_workgroup_variants():
         assert status_of(big_rows, variant="flash", ptrs=far) == 5
 
 
+def test_noalloc_entry_point_checks_before_touching_a_device():
+    """kb_attention_naive_noalloc: bad arguments and problems whose scores
+    exceed the static scratch are refused before any device query or launch;
+    a valid call without a device reports KB_ERR_NO_DEVICE."""
+    lib = kb.lib()
+    ptrs = (FAKE, FAKE * 2, FAKE * 3, FAKE * 4)
+    assert lib.kb_attention_naive_noalloc(None, *ptrs, None) == 1
+    assert lib.kb_attention_naive_noalloc(ctypes.byref(cfg(dim=48)), *ptrs, None) == 2
+    big = cfg(batch=1, heads=2, seq=4096, dim=32)  # 2 * 4096^2 * 4 B = 128 MiB > 64 MiB
+    assert lib.kb_attention_naive_noalloc(ctypes.byref(big), *ptrs, None) == 3
+    assert b"static scratch" in lib.kb_last_error()
+    import torch
+    if not torch.cuda.is_available():
+        fits = cfg(batch=1, heads=1, seq=4096, dim=32)  # exactly 64 MiB
+        assert lib.kb_attention_naive_noalloc(ctypes.byref(fits), *ptrs, None) == 5
+
+
 def test_misaligned_or_overlapping_buffers():
     assert status_of(cfg(), ptrs=(FAKE + 2, FAKE * 2, FAKE * 3, FAKE * 4)) == 1
     # O overlapping Q

@@ -22,7 +22,7 @@ STATUS = {0: "KB_OK", 1: "KB_ERR_INVALID", 2: "KB_ERR_UNSUPPORTED", 3: "KB_ERR_W
 SIZE_MAX = 2 ** (8 * ctypes.sizeof(ctypes.c_size_t)) - 1
 
 # Every symbol the header declares (checked by the CPU tests).
-EXPORTS = ("kb_attention", "kb_attention_workspace_size", "kb_triad", "kb_bench_attention",
+EXPORTS = ("kb_attention", "kb_attention_naive_noalloc", "kb_attention_workspace_size", "kb_triad", "kb_bench_attention",
            "kb_bench_triad", "kb_bench_stream", "kb_ceiling_work_size", "kb_bench_ceiling", "kb_device_info",
            "kb_status_string", "kb_last_error")
 CEILINGS = {"mfma_bf16": 0, "mfma_f32": 1, "fma_f32": 2, "exp_f32": 3, "lds_read": 4, "l1_read": 5, "l2_read": 6,
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         fp = ctypes.POINTER(ctypes.c_float)
         h.kb_attention.argtypes = [cfgp, vp, vp, vp, vp, i32, vp]
         h.kb_attention.restype = i32
+        h.kb_attention_naive_noalloc.argtypes = [cfgp, vp, vp, vp, vp, vp]
+        h.kb_attention_naive_noalloc.restype = i32
         h.kb_attention_workspace_size.argtypes = [cfgp, i32]
         h.kb_attention_workspace_size.restype = sz
         h.kb_triad.argtypes = [vp, vp, vp, f32, sz, i32, vp]
@@ -110,6 +112,16 @@ def _variant(v) -> int:
 def kb_attention(cfg: KbAttnCfg, q: int, k: int, v: int, o: int, variant, stream: int = 0) -> None:
     _check(lib().kb_attention(ctypes.byref(cfg), q, k, v, o, _variant(variant), stream or None),
            "kb_attention")
+
+
+def kb_attention_naive_noalloc(cfg: KbAttnCfg, q: int, k: int, v: int, o: int, stream: int = 0) -> None:
+    _check(lib().kb_attention_naive_noalloc(ctypes.byref(cfg), q, k, v, o, stream or None),
+           "kb_attention_naive_noalloc")
+
+
+# Bytes of the library's static scratch behind kb_attention_naive_noalloc
+# (KB_NOALLOC_SCRATCH_BYTES in the header).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def kb_attention_workspace_size(cfg: KbAttnCfg, variant) -> int:

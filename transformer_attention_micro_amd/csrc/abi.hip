@@ -10,10 +10,19 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kb_attention.h"
 #include "kb_device.hpp"
+
+// Device scratch of kb_attention_naive_noalloc: the naive variant's fp32
+// score matrix lives here instead of in a caller-provided workspace.  Every
+// GPU the library runs on holds its own copy from the code object's load
+// until the process ends.  Host code never uses this name as an address
+// (on the host it is only a stand-in for the symbol): the device address
+// comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[KB_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -282,9 +291,64 @@ kb_status bench_loop(F fn, hipStream_t stream, int32_t warmup, int32_t iters, fl
   return st;
 }
 
+// Per-device address of `scratch`, looked up on the first call on each
+// device (with that device current) and kept.
+std::atomic<void *> g_scratch[kMaxDev];
+std::mutex g_scratch_mu;
+
+kb_status scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_err("hipGetDevice: %s", hipGetErrorString(e));
+    return KB_ERR_NO_DEVICE;
+  }
+  if (dev < 0 || dev >= kMaxDev) {
+    set_err("device id %d out of range", dev);
+    return KB_ERR_NO_DEVICE;
+  }
+  void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                   "hipGetSymbolAddress(scratch)");
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return KB_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+kb_status kb_attention_naive_noalloc(const kb_attn_cfg *cfg, const void *Q, const void *K, const void *V,
+                                     void *O, void *stream) {
+  kb_problem p;
+  kb_status st = validate(cfg, KB_NAIVE, &p);
+  if (st != KB_OK) return st;
+  const size_t need = naive_ws_bytes(p);
+  if (need > (size_t)KB_NOALLOC_SCRATCH_BYTES) {
+    set_err("naive needs %zu bytes of scores (batch*heads*seq*seq*4); the static scratch holds %zu",
+            need, (size_t)KB_NOALLOC_SCRATCH_BYTES);
+    return KB_ERR_WORKSPACE;
+  }
+  st = device_check(nullptr);
+  if (st != KB_OK) return st;
+  void *ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != KB_OK) return st;
+  kb_attn_cfg c = *cfg;
+  c.workspace = ws;
+  c.workspace_bytes = KB_NOALLOC_SCRATCH_BYTES;
+  st = prepare(&c, Q, K, V, O, KB_NAIVE, stream, &p);
+  if (st != KB_OK) return st;
+  return launch(p, KB_NAIVE);
+}
 
 kb_status kb_attention(const kb_attn_cfg *cfg, const void *Q, const void *K, const void *V, void *O,
                        int32_t variant, void *stream) {
