@@ -196,6 +196,18 @@ def test_flash_several_units_per_workgroup(causal):
         full_check(p, "flash", f"B{B}H{H}S{S}/d{d}/{'c' if causal else 'nc'}/flash")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_flash_f32_both_kernels(causal):
+    """fp32 flash takes the 128-query tile kernel once its grid covers the
+    CUs (B*H*ceil(S/128) >= 256 here) and the key-split kernel on 16-query
+    blocks below that: shapes on both sides of the switch, every d, ragged
+    tails, checked on every element."""
+    for (B, H, S, d) in ((2, 16, 1100, 64), (4, 16, 520, 128), (8, 32, 200, 32),  # tile kernel
+                         (1, 15, 1100, 64), (2, 3, 520, 128), (1, 1, 2000, 32)):  # key-split kernel
+        p = inputs.make_problem(B, H, S, d, inputs.F32, causal=causal, seed=B * H + S + d)
+        full_check(p, "flash", f"f32/B{B}H{H}S{S}/d{d}/{'c' if causal else 'nc'}/flash")
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_bf16_output(variant):
     """out_dtype bf16 is the fp32 result rounded to nearest even: bit-exact

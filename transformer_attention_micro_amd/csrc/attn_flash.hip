@@ -8,10 +8,14 @@
 // the sequence length.
 //
 // gfx950 design (not the page's scalar design):
-//  * Each wave owns 32 query rows.  bf16: a workgroup is 8 waves (256 queries
-//    of one (batch, head) slice), two per SIMD, alone on its CU; fp32: 4
-//    waves (128 queries).
-//  * Both contractions run on MFMA 32x32 tiles, computed transposed:
+//  * bf16: each wave owns 32 query rows; a workgroup is 8 waves (256 queries
+//    of one (batch, head) slice), two per SIMD, alone on its CU.  fp32: when
+//    128-query workgroups would leave CUs idle, a workgroup is several waves
+//    on one block of 16 queries, each wave taking a part of the keys, the
+//    partial results merged through LDS (so even small problems fill the
+//    chip); otherwise 4 waves of 32 queries share K/V tiles in LDS.
+//  * Both contractions run on MFMA tiles (bf16 32x32, fp32 16x16 or 32x32),
+//    computed transposed:
 //      S^T = K Q^T   (A = K tile from LDS, B = Q^T kept in VGPRs)
 //      O^T += V^T P^T (A = V^T read from LDS with the transposing ds_read,
 //                      B = P^T straight from the S^T accumulator registers)
@@ -21,7 +25,7 @@
 //    O^T is a per-lane scalar.
 //  * bf16 inputs: bf16 MFMA (32x32x16), fp32 accumulate, the probabilities
 //    rounded to bf16 (round to nearest even) for P V.  fp32 inputs: fp32
-//    MFMA (32x32x2) and fp32 probabilities throughout.
+//    MFMA (16x16x4 or 32x32x2) and fp32 probabilities throughout.
 //  * The logit scale is applied in fp32 to the fp32 dot products, folded
 //    with log2(e) so that one v_exp_f32 (2^x) gives the exponential.  (It is
 //    not folded into Q: rounding the scaled Q to bf16 errs in proportion to
@@ -30,8 +34,10 @@
 //    a persistent grid walks an XCD-aware list of query tiles.  The row sums
 //    of the steady tiles are taken by small MFMAs from the bf16
 //    probabilities, which keeps an add per score off the vector ALU.
-//    fp32: K/V tiles are double-buffered in LDS through registers (the loads
-//    of tile t+1 are issued before tile t is computed) on a dispatched grid.
+//    fp32, key-split: each wave reads its K/V blocks straight from global
+//    memory into MFMA operand registers (no tile is shared between its
+//    waves); fp32, tiles: K/V tiles double-buffered in LDS through
+//    registers.  Both on a dispatched grid.
 //  * O and l share a reference m that need not be the running maximum (O / l
 //    does not depend on it in exact arithmetic).  bf16: the first, diagonal,
 //    ragged and last tiles take the exact row maximum; the others take none
@@ -55,7 +61,6 @@ using namespace kb;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBr = 128;  // queries per workgroup (fp32 kernel)
 // Growth of a row maximum (log2 units) tolerated before rescaling.
 constexpr float kRescaleLog2 = 8.0f;
 // Largest per-lane sum of a steady tile's probabilities, taken against the
@@ -772,12 +777,175 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
 }
 
 // ------------------------------------------------------------------- fp32 ---
-// Same structure with 32-key tiles and the fp32 MFMA (contraction 2 per
-// instruction).  The contraction index is permuted consistently on both
-// operands: step (g, e) uses d-columns 8g + 4h + e from lane half h, so each
-// lane reads 16-byte vectors.  P^T slot c of a lane is key acc_row(c, h).
+// fp32 inputs, small grids: 16-query blocks on the 16x16x4 fp32 MFMA, so
+// that small problems still spread over every CU.  A workgroup is NW waves
+// on one block of 16 queries; wave w takes the w-th of NW parts of the
+// block's visible keys (in 16-key blocks), runs the online softmax over it,
+// and the partial results (m_w, l_w, O_w) are merged through LDS by the same
+// identity that merges the tiles of one wave: m = max m_w,
+// l = sum 2^(m_w - m) l_w, O = sum 2^(m_w - m) O_w / l.
+//   S^T = K Q^T:  A = K (row = key, lane % 16), B = Q^T (column = query,
+//                 lane % 16), contraction step (c, e) on d-column
+//                 16 c + 4 (lane / 16) + e, so each lane reads 16-byte
+//                 vectors of K and Q.  Lane l then holds the scores of query
+//                 l % 16 against keys 4 (l / 16) + i, i = 0..3, of the block.
+//   O^T += V^T P^T: contraction step s on keys 4 g + s (g = lane / 16), so
+//                 the B operand of step s is the lane's own probability i = s;
+//                 A = V^T, lane l providing V[key 4 g + s][16 c + l % 16].
+//                 Lane l accumulates O^T[d = 16 c + 4 (l / 16) + i][query l % 16].
+// The next block's scores are computed before the current block's softmax,
+// so the matrix core has independent work while the vector ALU runs.
+constexpr int kQb = 16;  // queries per workgroup of the key-split kernel
+// Waves (key parts) per workgroup of the key-split kernel: two per SIMD, so
+// one wave's softmax overlaps the other's products (8 measured 12 % faster
+// than 4 at B1 H8 S512 d64).
+constexpr int kSplitWaves = 8;
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) void flash_f32_split_kernel(const float *__restrict__ Q,
+                                                                  const float *__restrict__ K,
+                                                                  const float *__restrict__ V,
+                                                                  void *__restrict__ O, int out_bf16, int S,
+                                                                  int nbh, int nqt, float sl2e) {
+  constexpr int G = D / 16;  // 16-wide column groups of d
+  __shared__ float part_o[NW][G][16][kQb];  // [wave][column group][d % 16][query]
+  __shared__ float part_m[NW][kQb], part_l[NW][kQb];
+
+  int bh, qt;
+  if (!tile_of_block(bh, qt, nbh, nqt, CAUSAL)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int q0 = qt * kQb, q = q0 + n;
+  const size_t base = (size_t)bh * S * D;
+
+  f32x4 qf[G];
+  {
+    const float *qp = Q + base + (size_t)min(q, S - 1) * D + 4 * g;
+#pragma unroll
+    for (int c = 0; c < G; ++c) qf[c] = *(const f32x4 *)(qp + 16 * c);
+  }
+  // This wave's 16-key blocks [b0, b1) of the block's visible range.
+  const int kend = CAUSAL ? min(S, q0 + kQb) : S;
+  const int nblk = (kend + 15) / 16;
+  const int per = (nblk + NW - 1) / NW;
+  const int b0 = min(nblk, w * per), b1 = min(nblk, b0 + per);
+
+  f32x4 oacc[G];
+#pragma unroll
+  for (int c = 0; c < G; ++c) oacc[c] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;  // l_run: this lane's share (its 4 keys per block)
+
+  // Scores of block b (raw dot products): two accumulators for two
+  // independent MFMA chains, added at the end.
+  auto scores = [&](int b) KB_INLINE {
+    const float *kp = K + base + (size_t)min(16 * b + n, S - 1) * D + 4 * g;
+    f32x4 kf[G];
+#pragma unroll
+    for (int c = 0; c < G; ++c) kf[c] = *(const f32x4 *)(kp + 16 * c);
+    f32x4 s0 = f32x4{}, s1 = f32x4{};
+#pragma unroll
+    for (int c = 0; c < G; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (((c * 4 + e) & 1) == 0) s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[c][e], qf[c][e], s0, 0, 0, 0);
+        else s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[c][e], qf[c][e], s1, 0, 0, 0);
+      }
+    return s0 + s1;
+  };
+
+  f32x4 snext = b0 < b1 ? scores(b0) : f32x4{};
+  for (int b = b0; b < b1; ++b) {
+    const f32x4 sraw = snext;
+    // V^T operands of this block (loaded before the next block's scores).
+    float vf[4][G];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float *vp = V + base + (size_t)min(16 * b + 4 * g + s4, S - 1) * D + n;
+#pragma unroll
+      for (int c = 0; c < G; ++c) vf[s4][c] = vp[16 * c];
+    }
+    if (b + 1 < b1) snext = scores(b + 1);
+    // Mask (ragged end of the sequence; causal: keys after the query), scale
+    // to log2 units, row max over the lane's 4 keys and the 4 lane groups.
+    const int kb = 16 * b + 4 * g;
+    const bool need_mask = (16 * b + 16 > S) || (CAUSAL && 16 * b + 15 > q0);
+    float x[4], mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = sraw[i] * sl2e;
+      if (need_mask && (kb + i >= S || (CAUSAL && kb + i > q))) x[i] = -INFINITY;
+      mt = fmaxf(mt, x[i]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = exp2_fast(m_run - m_new);
+    m_run = m_new;
+    float p[4], ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2_fast(x[i] - m_new);
+      ls += p[i];
+    }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int c = 0; c < G; ++c) oacc[c] *= alpha;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int c = 0; c < G; ++c) oacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[s4][c], p[s4], oacc[c], 0, 0, 0);
+  }
+
+  // Merge the waves' partial results.  The row sum over the 4 lane groups
+  // first (every group holds the same reference m_run).
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (g == 0) {
+    part_m[w][n] = m_run;
+    part_l[w][n] = l_run;
+  }
+#pragma unroll
+  for (int c = 0; c < G; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part_o[w][c][4 * g + i][n] = oacc[c][i];
+  __syncthreads();
+  // Wave w finishes the column groups c = w, w + NW, ...: lane (g, n) the
+  // four d-columns 16 c + 4 g .. + 3 of query n.
+  float mw[NW], m_all = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    mw[v] = part_m[v][n];
+    m_all = fmaxf(m_all, mw[v]);
+  }
+  float l_all = 0.f, sc[NW];
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    sc[v] = exp2_fast(mw[v] - m_all);  // 0 for a wave with no keys (m = -inf)
+    l_all += sc[v] * part_l[v][n];
+  }
+  const float inv = 1.f / l_all;
+  for (int c = w; c < G; c += NW) {
+    f32x4 o4 = f32x4{};
+#pragma unroll
+    for (int v = 0; v < NW; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] += sc[v] * part_o[v][c][4 * g + i][n];
+    if (q < S) store_out4(O, base + (size_t)q * D + 16 * c + 4 * g, o4 * inv, out_bf16);
+  }
+}
+
+// fp32 inputs, large grids: 128 queries per workgroup (4 waves of 32), the
+// K/V tiles (32 keys) staged in LDS once for all of them and double-
+// buffered through registers (the loads of tile t+1 are issued before tile
+// t is computed); 32x32x2 fp32 MFMAs.  The contraction index is permuted
+// consistently on both operands: step (g, e) uses d-columns 8g + 4h + e
+// from lane half h, so each lane reads 16-byte vectors.  P^T slot c of a
+// lane is key acc_row(c, h).  Used when its grid already covers the CUs;
+// smaller problems take the key-split kernel above.
+constexpr int kBr = 128;  // queries per workgroup of the tile kernel
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void flash_f32_kernel(const float *__restrict__ Q,
+__global__ __launch_bounds__(kThreads) void flash_f32_tile_kernel(const float *__restrict__ Q,
                                                              const float *__restrict__ K,
                                                              const float *__restrict__ V,
                                                              void *__restrict__ O, int out_bf16, int S, int nbh,
@@ -931,7 +1099,10 @@ int cu_count() {
 
 template <int D, bool CAUSAL>
 hipError_t launch_d(const kb_problem &p) {
-  const int br = p.bf16 ? kBrB : kBr;
+  // fp32: the tile kernel once its 128-query grid covers every CU, else the
+  // key-split kernel on 16-query blocks.
+  const bool split = !p.bf16 && (long long)p.bh * ((p.S + kBr - 1) / kBr) < cu_count();
+  const int br = p.bf16 ? kBrB : split ? kQb : kBr;
   const int nqt = (p.S + br - 1) / br;
   // kXcds workgroups per item of the longest per-XCD list (see tile_of_block).
   const long long per = (long long)((p.bh + kXcds - 1) / kXcds) * nqt;
@@ -947,8 +1118,12 @@ hipError_t launch_d(const kb_problem &p) {
     hipLaunchKernelGGL((flash_bf16_kernel<D, CAUSAL>), grid_b, dim3(kThreadsB), 0, p.stream,
                        (const bf16_t *)p.Q, (const bf16_t *)p.K, (const bf16_t *)p.V, p.O, p.out_bf16, p.S, p.bh,
                        nqt, sl2e);
+  else if (split)
+    hipLaunchKernelGGL((flash_f32_split_kernel<D, CAUSAL, kSplitWaves>), grid, dim3(64 * kSplitWaves), 0, p.stream,
+                       (const float *)p.Q, (const float *)p.K, (const float *)p.V, p.O, p.out_bf16, p.S, p.bh,
+                       nqt, sl2e);
   else
-    hipLaunchKernelGGL((flash_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, p.stream,
+    hipLaunchKernelGGL((flash_f32_tile_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, p.stream,
                        (const float *)p.Q, (const float *)p.K, (const float *)p.V, p.O, p.out_bf16, p.S, p.bh,
                        nqt, sl2e);
   return hipGetLastError();
