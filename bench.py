@@ -26,8 +26,8 @@ The JSON line also carries:
                 mask) x every variant (flash, naive, fused): min / p50 / p99
                 / mean kernel time, TFLOP/s and the fraction of the dtype's
                 MFMA peak, algorithmic GB/s and the fraction of 8 TB/s, the
-                shader clock and socket power sampled during the timed
-                launches, and the max-abs / relative-L2 error against the
+                shader clock right before and right after the timed launches
+                (a short clock probe), and the max-abs / relative-L2 error against the
                 oracle (filled in by the CPU leg; every row for S <= 2048,
                 the tile-edge rows plus 64 seeded rows per head above);
                 a variant that cannot run a workload says why;
@@ -50,7 +50,6 @@ import json
 import os
 import subprocess
 import sys
-import threading
 import time
 
 import numpy as np
@@ -99,66 +98,46 @@ def device_tensors(p, torch):
 
 # ---------------------------------------------------------------- clocks
 
-class ClockSampler:
-    """Samples the GPU's shader clock (mean over the XCDs) and socket power
-    through amdsmi in a background thread while a measurement runs.  Without
-    amdsmi access every field is None and `error` says why."""
+class ClockProbe:
+    """The shader clock right before and right after a measurement, from a
+    ~40 us launch of the fp32-FMA ceiling probe (its waves time themselves
+    with s_memtime against the 100 MHz s_memrealtime; kb_bench_ceiling).
+    The SMU's own metrics (amdsmi) refresh about once a second, too slowly
+    for rows that run a fraction of a second, so they give only the socket
+    power of the last refresh."""
 
-    def __init__(self, period_s: float = 0.01):
-        self.period = period_s
-        self.error = None
-        self.handle = None
+    def __init__(self, kb, torch, stream, iters: int = 2000):
+        self.kb, self.stream, self.iters = kb, stream, iters
+        self.work = torch.empty(kb.kb_ceiling_work_size(), dtype=torch.uint8, device="cuda")
+        self.smu = None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
             self.amdsmi = amdsmi
-            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
-            self.read()
-        except Exception as e:  # no driver access: report, do not fail the bench
-            self.error = f"{type(e).__name__}: {e}"
-            self.handle = None
+            self.smu = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:  # no SMU access: report the probe clocks only
+            self.smu = None
 
-    def read(self):
-        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
-        clks = m.get("current_gfxclks")
-        vals = [c for c in clks if isinstance(c, (int, float)) and 0 < c < 10000] if isinstance(clks, list) else []
-        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
-            vals = [m["current_gfxclk"]]
-        pw = m.get("current_socket_power")
-        return (float(np.mean(vals)) if vals else None, float(pw) if isinstance(pw, (int, float)) else None)
+    def mhz(self):
+        _, _, mhz = self.kb.kb_bench_ceiling("fma_f32", self.iters, self.work.data_ptr(), self.work.numel(),
+                                             self.stream, 0, 1)
+        return round(mhz, 0)
 
-    def __enter__(self):
-        self.samples = []
-        self._stop = threading.Event()
-        if self.handle is not None:
-            self._t = threading.Thread(target=self._run, daemon=True)
-            self._t.start()
-        return self
+    def smu_power(self):
+        if self.smu is None:
+            return None
+        try:
+            pw = self.amdsmi.amdsmi_get_gpu_metrics_info(self.smu).get("current_socket_power")
+            return float(pw) if isinstance(pw, (int, float)) else None
+        except Exception:
+            return None
 
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self.read())
-            except Exception as e:
-                self.error = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(self.period)
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self.handle is not None:
-            self._t.join()
-        return False
-
-    def summary(self):
-        clk = [c for c, _ in self.samples if c is not None]
-        pw = [p for _, p in self.samples if p is not None]
-        if not clk:
-            return {"gfx_mhz_mean": None, "error": self.error or "no samples"}
-        return {"gfx_mhz_mean": round(float(np.mean(clk)), 0), "gfx_mhz_min": round(min(clk), 0),
-                "gfx_mhz_max": round(max(clk), 0), "gfx_mhz_first": round(clk[0], 0),
-                "gfx_mhz_last": round(clk[-1], 0),
-                "socket_power_w_mean": round(float(np.mean(pw)), 0) if pw else None, "samples": len(clk)}
+    def around(self, fn):
+        """Runs fn() between two probe launches; returns (fn's result, clocks)."""
+        before = self.mhz()
+        out = fn()
+        after = self.mhz()
+        return out, {"shader_mhz_before": before, "shader_mhz_after": after, "smu_socket_power_w": self.smu_power()}
 
 
 # ---------------------------------------------------------------- timing helpers
@@ -190,7 +169,7 @@ def algorithmic_bytes(kb, p, variant):
     return comp + (16 * p.BH * p.S * p.S if variant == "naive" else 0)
 
 
-def per_config_table(kb, torch, inputs, stream, cache, sampler, checks, variants=("flash", "naive", "fused"),
+def per_config_table(kb, torch, inputs, stream, cache, clocks, checks, variants=("flash", "naive", "fused"),
                      flash_iters=100, warm_ms=300.0, budget_ms=600.0):
     """Every configured workload x variant x mask.  flash first (each row
     warmed for >= warm_ms, so none sits in a clock transient; before the
@@ -229,8 +208,8 @@ def per_config_table(kb, torch, inputs, stream, cache, sampler, checks, variants
                         else:
                             warm, iters = 1, int(min(100, max(3, budget_ms / t1)))
                         kb.kb_bench_attention(cfg, *ptrs, variant, stream, warm, 1)
-                        with sampler:
-                            per, _ = kb.kb_bench_attention(cfg, *ptrs, variant, stream, 0, iters)
+                        (per, _), clk = clocks.around(
+                            lambda: kb.kb_bench_attention(cfg, *ptrs, variant, stream, 0, iters))
                         st = time_stats(per)
                         fl = kb.attention_flops(p.B, p.H, p.S, p.d, causal)
                         nb = algorithmic_bytes(kb, p, variant)
@@ -240,7 +219,7 @@ def per_config_table(kb, torch, inputs, stream, cache, sampler, checks, variants
                                     "frac_of_peak": round(tf / PEAK_TFLOPS[p.dtype], 4),
                                     "tflops_at_mean": round(fl / (st["mean"] * 1e-3) / 1e12, 2),
                                     "algorithmic_bytes": nb, "gbs": round(gbs, 1),
-                                    "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4), "clock": sampler.summary(),
+                                    "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4), "clock": clk,
                                     "max_abs_err": None, "rel_l2_err": None})
                         torch.cuda.synchronize()
                         got = o.cpu().numpy().reshape(p.BH * p.S, p.d)
@@ -473,16 +452,14 @@ def main():
     stream = int(torch.cuda.current_stream().cuda_stream)
     flops = kb.attention_flops(p.B, p.H, p.S, p.d, p.causal)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
-    sampler = ClockSampler()
-
     for _ in range(args.warmup):
         kb.kb_attention(cfg, *ptrs, "flash", stream)
     torch.cuda.synchronize()
-    with sampler:
-        t0 = time.perf_counter()
-        per, total_ms = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, 0, args.steps)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    per, total_ms = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, 0, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    clocks = ClockProbe(kb, torch, stream)  # after the timed steps: the probe must not warm them
     ms_per_step = wall * 1e3 / args.steps
     kern_ms = float(np.mean(per))
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -512,7 +489,7 @@ def main():
                      "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_min": round(float(np.min(per)), 4),
                      "kernel_ms_p50": round(float(np.median(per)), 4),
                      "kernel_ms_p99": round(float(np.percentile(per, 99)), 4),
-                     "clock": sampler.summary()},
+                     "shader_mhz_after": clocks.mhz()},
     }
     if args.warmup < 100:
         result["roofline"]["note"] = (f"{args.warmup} warmup launches leave the timed ones inside the clock "
@@ -526,7 +503,7 @@ def main():
     cache = {args.workload: p}
     if not args.no_configs:
         variants = ("flash",) if args.flash_only else ("flash", "naive", "fused")
-        result["per_config"] = per_config_table(kb, torch, inputs, stream, cache, sampler, checks, variants)
+        result["per_config"] = per_config_table(kb, torch, inputs, stream, cache, clocks, checks, variants)
 
     if args.copy_mib > 0:
         n = args.copy_mib * (1 << 20) // 4

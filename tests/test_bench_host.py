@@ -1,6 +1,6 @@
 """Host-side helpers of bench.py (no GPU): timing statistics, the rows the
 oracle checks, algorithmic bytes per variant, the host CPU description and
-the clock sampler's behaviour without GPU metrics."""
+the clock probe around a measured call."""
 import numpy as np
 
 import bench
@@ -43,11 +43,33 @@ def test_host_cpu_reports_cores():
         assert info["smt_threads_per_core"] is None or info["smt_threads_per_core"] >= 1
 
 
-def test_clock_sampler_degrades_without_gpu_metrics():
-    s = bench.ClockSampler(period_s=0.001)
-    with s:
-        pass
-    out = s.summary()
-    assert "gfx_mhz_mean" in out
-    if s.handle is None:
-        assert out["gfx_mhz_mean"] is None and out["error"]
+def test_clock_probe_reads_the_probe_clock_around_a_call():
+    """ClockProbe.around runs the call between two probe readings (a stand-in
+    library object here; the real probe needs a GPU)."""
+    calls = []
+
+    class FakeKb:
+        def kb_ceiling_work_size(self):
+            return 16
+
+        def kb_bench_ceiling(self, kind, iters, work, n, stream, warmup, reps):
+            calls.append(kind)
+            return [0.04], 1.0, 1700.0 + len(calls)
+
+    class FakeTorch:
+        uint8 = None
+
+        @staticmethod
+        def empty(n, dtype=None, device=None):
+            class T:
+                def data_ptr(self):
+                    return 1
+
+                def numel(self):
+                    return n
+            return T()
+
+    probe = bench.ClockProbe(FakeKb(), FakeTorch(), 0)
+    out, clk = probe.around(lambda: "ran")
+    assert out == "ran" and calls == ["fma_f32", "fma_f32"]
+    assert clk["shader_mhz_before"] == 1701.0 and clk["shader_mhz_after"] == 1702.0
