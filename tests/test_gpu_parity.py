@@ -208,6 +208,22 @@ def test_flash_f32_both_kernels(causal):
         full_check(p, "flash", f"f32/B{B}H{H}S{S}/d{d}/{'c' if causal else 'nc'}/flash")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_flash_bf16_both_widths(causal):
+    """bf16 flash runs 8-wave workgroups on 256-query items, or 4-wave ones
+    on 128-query items when ceil(B*H/8) times the 256-query units per slice
+    (ceil(S/256), halved up when causal) is below the 32 CUs of an XCD:
+    shapes on both sides of that switch, every d, ragged tails, and d=64
+    shapes with more 128-query units than CUs (two workgroups per CU),
+    checked on every element."""
+    shapes = ((1, 16, 2048, 64), (1, 8, 1100, 128), (2, 5, 700, 32),  # 4 waves
+              (4, 30, 300, 64), (2, 60, 700, 64),                     # 4 waves, two per CU
+              (2, 16, 4096, 64), (1, 64, 1800, 128), (4, 64, 260, 32))  # 8 waves
+    for (B, H, S, d) in shapes:
+        p = inputs.make_problem(B, H, S, d, inputs.BF16, causal=causal, seed=B * H + S + d)
+        full_check(p, "flash", f"bf16/B{B}H{H}S{S}/d{d}/{'c' if causal else 'nc'}/flash")
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_bf16_output(variant):
     """out_dtype bf16 is the fp32 result rounded to nearest even: bit-exact

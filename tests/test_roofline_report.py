@@ -10,7 +10,7 @@ import pytest
 
 from transformer_attention_micro_amd import roofline as rl
 
-FLASH = "void (anonymous namespace)::flash_bf16_kernel<128, true>(bool _Accum const*, _S, _P, void, int, float)"
+FLASH = "void (anonymous namespace)::flash_bf16_kernel<128, true, 8>(bool _Accum const*, _S, _P, void, int, float)"
 SOFTMAX = "_ZN12_GLOBAL__N_118softmax_vec_kernelEPfii"
 READ = "(anonymous namespace)::read_vec_kernel(float*, HIP_vector_type<float, 4u> const*, float, unsigned long)"
 WRITE = "(anonymous namespace)::write_vec_kernel(HIP_vector_type<float, 4u>*, float, unsigned long)"
@@ -103,6 +103,10 @@ def _load(d):
 
 def test_kernel_names_map_to_labels():
     assert rl.label_of(FLASH) == "flash"
+    for fp32 in ("void (anonymous namespace)::flash_f32_split_kernel<64, false, 8>(float const*, float const*, "
+                 "float const*, void*, int, int, int, int, float)",
+                 "_ZN12_GLOBAL__N_121flash_f32_tile_kernelILi64ELb1EEEvPKfS2_S2_Pviiiif"):
+        assert rl.label_of(fp32) == "flash", fp32
     assert rl.label_of(SOFTMAX) == "naive 2/3 softmax"
     assert rl.label_of(L1P) == "L1 read probe"
     assert rl.label_of(LDSP) == "LDS read probe"

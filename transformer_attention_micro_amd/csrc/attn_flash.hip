@@ -9,7 +9,8 @@
 //
 // gfx950 design (not the page's scalar design):
 //  * bf16: each wave owns 32 query rows; a workgroup is 8 waves (256 queries
-//    of one (batch, head) slice), two per SIMD, alone on its CU.  fp32: when
+//    of one (batch, head) slice), two per SIMD, alone on its CU, or 4 waves
+//    (128 queries) when 256-query items would leave CUs idle.  fp32: when
 //    128-query workgroups would leave CUs idle, a workgroup is several waves
 //    on one block of 16 queries, each wave taking a part of the keys, the
 //    partial results merged through LDS (so even small problems fill the
@@ -150,11 +151,14 @@ __device__ __forceinline__ void pin(T &x) {
   asm volatile("" : "+v"(x));
 }
 
-// bf16 kernel.  A workgroup is 8 waves, two per SIMD, each owning 32 query
-// rows, so it covers 256 queries of one head; its LDS ring (128 KiB) keeps
-// it alone on its CU, and every K/V tile staged there feeds 256 queries.
-// While one wave of a SIMD waits at a barrier or on an LDS read, the other
-// keeps the matrix core busy.  Per 64-key tile step t a wave has three pieces of
+// bf16 kernel.  A workgroup is NW = 8 waves, two per SIMD, each owning 32
+// query rows, so it covers 256 queries of one head; its LDS ring (128 KiB at
+// d = 128) keeps it alone on its CU, and every K/V tile staged there feeds
+// 256 queries.  While one wave of a SIMD waits at a barrier or on an LDS
+// read, the other keeps the matrix core busy.  Problems with fewer 256-query
+// work units than CUs take NW = 4 (128 queries per item, twice the units):
+// the same code, each K/V tile feeding half as many queries, on twice as
+// many CUs (two such workgroups share a CU where their rings fit in LDS).  Per 64-key tile step t a wave has three pieces of
 // work:
 //   O^T += V(t-1)^T P(t-1)^T    (MFMA, V from LDS, P from registers)
 //   softmax of tile t           (vector ALU: exponentials, bf16 P; a row
@@ -172,8 +176,6 @@ __device__ __forceinline__ void pin(T &x) {
 // LDS: rings of kStages K tiles and kStages V tiles filled by direct
 // global->LDS loads; step t issues K(t+4) and V(t+2), and waits (before its
 // barrier) for the loads of step t-3, which hold K(t+1) and V(t-1).
-constexpr int kBrB = 256;
-constexpr int kThreadsB = 512;
 constexpr int kStages = 4;
 
 // s_waitcnt immediate for vmcnt(n), n < 64, other counters left alone.
@@ -183,15 +185,15 @@ constexpr int wait_vm_lgkm_imm(int n, int l) { return (wait_vm_imm(n) & ~0x0F00)
 // Operand fragments each wave reads ahead of its MFMAs.
 constexpr int kPre = 4;
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bf16_kernel(
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bf16_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
     void *__restrict__ O, int out_bf16, int S, int nbh, int nqt, float sl2e) {
   constexpr int BC = 64;                 // keys per tile
   constexpr int KC = D / 16;             // bf16 MFMA steps along d for S^T
   constexpr int MB = D / 32;             // 32-row blocks of O^T
   constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int NW = kThreadsB / 64;     // waves
+  constexpr int BR = 32 * NW;            // queries per item (32 per wave)
   constexpr int NI = BC * CPR / 64;      // 1 KiB direct-load instructions per tile
   constexpr int CHW = (NI + NW - 1) / NW;  // of which each wave issues (or none)
   constexpr int NPV = 4 * MB;            // MFMAs of P V per tile
@@ -205,7 +207,8 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
   auto kst = [&](int j) KB_INLINE { return (lds_bf16 *)(ring + j * BC * D); };
   auto vst = [&](int j) KB_INLINE { return (lds_bf16 *)(ring + (kStages + j) * BC * D); };
 
-  // Persistent schedule: the grid holds kXcds * nw workgroups (one per CU).
+  // Persistent schedule: the grid holds kXcds * nw workgroups (one per CU;
+  // 4-wave workgroups two per CU where both LDS rings fit).
   // Workgroup g runs on XCD x = g % 8 (workgroups are dealt round-robin to
   // the XCDs) as its j-th workgroup, j = g / 8.  XCD x owns the slices
   // [x hp, min(nbh, (x + 1) hp)), hp = ceil(nbh / 8), so each slice's K/V
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     // wave's tile range stay scalar.
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
-    const int q0 = qt * kBrB;
+    const int q0 = qt * BR;
     const int qw = q0 + 32 * w;
     const int q = qw + l32;
     const size_t base = (size_t)bh * S * D;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     float m_run = -INFINITY, l_run = 0.f;
     bool inexact = false;  // a steady tile's reference was stale beyond repair
 
-    const int kend = CAUSAL ? min(S, q0 + kBrB) : S;
+    const int kend = CAUSAL ? min(S, q0 + BR) : S;
     const int ntiles = (kend + BC - 1) / BC;
     // Tiles this wave computes: causal waves stop after the tile holding
     // their last query.  Query blocks start at multiples of 32 and tiles at
@@ -258,8 +261,9 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2, 2)
     // Direct global->LDS loads (buffer loads with the LDS flag).  Instruction
     // c of a tile fills bytes [1 KiB c, 1 KiB (c + 1)) of the stage; its lane
     // l writes physical 16-byte slot P = 64 c + l, which holds logical chunk
-    // (P % CPR) ^ f(row) of row P / CPR.  Wave w issues instructions w, w + 8,
-    // ... (at d = 32 a tile is 4 instructions and waves 4-7 issue none).  The
+    // (P % CPR) ^ f(row) of row P / CPR.  Wave w issues instructions w, w + NW,
+    // ... (at d = 32 a tile is 4 instructions, and with 8 waves waves 4-7
+    // issue none).  The
     // lane's byte offset within a tile is fixed (koff / voff) and the tile's
     // offset is a scalar, so a load costs no vector instructions.  The
     // buffer descriptors span this head's K and V exactly: rows past the end
@@ -1102,20 +1106,30 @@ hipError_t launch_d(const kb_problem &p) {
   // fp32: the tile kernel once its 128-query grid covers every CU, else the
   // key-split kernel on 16-query blocks.
   const bool split = !p.bf16 && (long long)p.bh * ((p.S + kBr - 1) / kBr) < cu_count();
-  const int br = p.bf16 ? kBrB : split ? kQb : kBr;
+  // bf16: persistent workgroups, one per CU at most, kXcds * nw in all (see
+  // the kernel's schedule), never more than there are work units.  8 waves
+  // on 256-query items unless that leaves CUs of an XCD without a unit, then
+  // 4 waves on 128-query items (two per CU where both LDS rings fit).
+  const int cus_x = std::max(1, cu_count() / kXcds);
+  const long long slices_x = (p.bh + kXcds - 1) / kXcds;
+  const bool narrow = p.bf16 && slices_x * causal_units((p.S + 255) / 256, CAUSAL) < cus_x;
+  const int br = p.bf16 ? (narrow ? 128 : 256) : split ? kQb : kBr;
   const int nqt = (p.S + br - 1) / br;
   // kXcds workgroups per item of the longest per-XCD list (see tile_of_block).
   const long long per = (long long)((p.bh + kXcds - 1) / kXcds) * nqt;
   if (per * kXcds > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(per * kXcds));
-  // bf16: persistent, one workgroup per CU at most, kXcds * nw in all (see
-  // the kernel's schedule), never more than there are work units.
-  const long long units = (long long)((p.bh + kXcds - 1) / kXcds) * (causal_units(nqt, CAUSAL));
-  const int nw = (int)std::max(1LL, std::min<long long>(units, std::max(1, cu_count() / kXcds)));
+  const long long units = slices_x * causal_units(nqt, CAUSAL);
+  const int per_cu = narrow && D <= 64 ? 2 : 1;
+  const int nw = (int)std::max(1LL, std::min<long long>(units, (long long)per_cu * cus_x));
   const dim3 grid_b((unsigned)(nw * kXcds));
   const float sl2e = p.scale * kLog2e;
-  if (p.bf16)
-    hipLaunchKernelGGL((flash_bf16_kernel<D, CAUSAL>), grid_b, dim3(kThreadsB), 0, p.stream,
+  if (p.bf16 && narrow)
+    hipLaunchKernelGGL((flash_bf16_kernel<D, CAUSAL, 4>), grid_b, dim3(256), 0, p.stream,
+                       (const bf16_t *)p.Q, (const bf16_t *)p.K, (const bf16_t *)p.V, p.O, p.out_bf16, p.S, p.bh,
+                       nqt, sl2e);
+  else if (p.bf16)
+    hipLaunchKernelGGL((flash_bf16_kernel<D, CAUSAL, 8>), grid_b, dim3(512), 0, p.stream,
                        (const bf16_t *)p.Q, (const bf16_t *)p.K, (const bf16_t *)p.V, p.O, p.out_bf16, p.S, p.bh,
                        nqt, sl2e);
   else if (split)

@@ -71,7 +71,7 @@ DATASHEET_HBM_GBS = 8000.0
 
 # Kernel-name patterns (demangled or mangled) -> label, in report order.
 KERNELS = [
-    (r"flash_bf16_kernel|flash_f32_kernel", "flash"),
+    (r"flash_(bf16|f32_split|f32_tile)_kernel", "flash"),
     (r"fused_kernel", "fused"),
     (r"scores_(bf16|f32)_kernel", "naive 1/3 scores"),
     (r"softmax_(vec|any)_kernel", "naive 2/3 softmax"),
