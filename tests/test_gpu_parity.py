@@ -257,8 +257,8 @@ def test_bf16_output(variant):
 # corrected in place), or by hundreds (the exponentials overflow and the
 # whole query tile is recomputed exactly).
 
-def _growing_keys(d, causal, jump, S=1024):
-    p = inputs.make_problem(1, 2, S, d, inputs.BF16, causal=causal, seed=11)
+def _growing_keys(d, causal, jump, S=1024, H=2):
+    p = inputs.make_problem(1, H, S, d, inputs.BF16, causal=causal, seed=11)
     j = np.arange(p.S)
     if jump:
         f = np.where(j >= 320, 256.0, 1.0)
@@ -279,6 +279,20 @@ def test_flash_scores_outgrowing_the_reference(d, causal, jump, S):
     o = run(p, "flash").cpu().numpy()
     want = oracle_full(p)
     compare(o, want, p.dtype, f"growing-keys/S{S}/d{d}/{'c' if causal else 'nc'}/{'jump' if jump else 'steps'}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("jump", [False, True])
+def test_flash_scores_outgrowing_the_reference_8_waves(d, causal, jump):
+    """The same growing keys on enough heads (64, or 128 causal, at S=1024)
+    that the kernel runs 8-wave workgroups on 256-query items: in-place
+    corrections and exact redos there, and (causal, d=64) the early output
+    stores of waves whose last tile comes before the item's last step."""
+    p = _growing_keys(d, causal, jump, 1024, H=128 if causal else 64)
+    o = run(p, "flash").cpu().numpy()
+    want = oracle_full(p)
+    compare(o, want, p.dtype, f"growing-keys-8w/H{p.H}/d{d}/{'c' if causal else 'nc'}/{'jump' if jump else 'steps'}")
 
 
 # A steady tile whose probabilities are each finite but whose sum is not: the

@@ -704,6 +704,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       rescale(grow, alpha);
     };
 
+    // This wave's 32 output rows, normalised, skipping rows past the end.
+    auto store_rows = [&]() KB_INLINE {
+      const float inv = 1.f / xor32_sum(l_run);
+      if (q < S) {
+        const size_t op = base + (size_t)q * D + 4 * h;
+  #pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const f32x4 o4 = {oacc[mb][4 * r] * inv, oacc[mb][4 * r + 1] * inv,
+                              oacc[mb][4 * r + 2] * inv, oacc[mb][4 * r + 3] * inv};
+            store_out4(O, op + 32 * mb + 8 * r, o4, out_bf16);
+          }
+      }
+    };
+    // Causal, d <= 64: a wave whose last tile comes before the item's last
+    // step stores its rows right after that tile's P V, during the steps in
+    // which the waves with later tiles finish (measured faster at d <= 64;
+    // at d = 128 the twice larger stores delay the idle wave's next
+    // barrier wait, which also counts them, and the item comes out slower).
+    constexpr bool kEarlyStore = CAUSAL && D <= 64;
+
     // One pass over the item's key tiles.  The exact pass takes every step
     // through `general` (a row maximum per tile); it runs only if the fast
     // pass met a tile whose reference was stale beyond repair.
@@ -736,7 +758,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
         if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
       }
-      for (; t <= ntiles; ++t) general(t);
+      for (; t <= ntiles; ++t) {
+        general(t);
+        // After step tw this wave's O and l are final.  A wave whose fast
+        // pass went inexact does not store (its item is redone and every
+        // wave stores again after the exact pass).
+        if (kEarlyStore && !exact && t == tw && !inexact) store_rows();
+      }
       // No tile load may still be writing this workgroup's LDS when it ends.
       __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
     };
@@ -747,7 +775,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     pass(false);
     if (inexact && lane == 0) redo_flag = 1;
     wg_barrier();
-    if (redo_flag != 0) {
+    const bool redone = redo_flag != 0;
+    if (redone) {
   #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
       m_run = -INFINITY;
@@ -755,19 +784,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       inexact = false;
       pass(true);
     }
-
-    const float inv = 1.f / xor32_sum(l_run);
-    if (q < S) {
-      const size_t op = base + (size_t)q * D + 4 * h;
-  #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-  #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 o4 = {oacc[mb][4 * r] * inv, oacc[mb][4 * r + 1] * inv,
-                            oacc[mb][4 * r + 2] * inv, oacc[mb][4 * r + 3] * inv};
-          store_out4(O, op + 32 * mb + 8 * r, o4, out_bf16);
-        }
-    }
+    if (!kEarlyStore || redone) store_rows();
   };
   for (int u = jw; u < hx * upd; u += nw) {
     const int bh = h0 + u / upd, r = u % upd;
