@@ -648,8 +648,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // t % 4) and V(t-2) (stage (t + 2) % 4), which are refilled with K(t+4)
     // and V(t+2); K(t+2) and V(t) are now readable, so the end of step t
     // reads the first fragments of step t+1 from them.
-    auto begin_step = [&](int t) KB_INLINE {
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm_imm(2 * CHW, 2 * kPre));
+    // `relax`: the wave issued its 4 MB output stores at the end of step
+    // t-1 or t-2, after the loads this wait is for.  vmcnt counts loads and
+    // stores together and retires them in issue order, so allowing those
+    // stores to stay outstanding still leaves the wanted loads complete.
+    auto begin_step = [&](int t, bool relax = false) KB_INLINE {
+      if (relax)
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm_imm(2 * CHW + 4 * MB, 2 * kPre));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm_imm(2 * CHW, 2 * kPre));
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -685,9 +692,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // Any step, buffers chosen at run time: the first, the last two of the
     // wave and the idle steps of causal waves that finished early (each wave
     // takes part in every step's barrier and loads).
-    auto general = [&](int t) KB_INLINE {
+    auto general = [&](int t, bool relax = false) KB_INLINE {
       const int st = t & 3;
-      begin_step(t);
+      begin_step(t, relax);
       load_tile(false, kst(st), t + 4);
       load_tile(true, vst((st + 2) & 3), t + 2);
       float alpha = 1.f;
@@ -719,12 +726,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           }
       }
     };
-    // Causal, d <= 64: a wave whose last tile comes before the item's last
-    // step stores its rows right after that tile's P V, during the steps in
-    // which the waves with later tiles finish (measured faster at d <= 64;
-    // at d = 128 the twice larger stores delay the idle wave's next
-    // barrier wait, which also counts them, and the item comes out slower).
-    constexpr bool kEarlyStore = CAUSAL && D <= 64;
+    // Causal: a wave whose last tile comes before the item's last step
+    // stores its rows right after that tile's P V, during the steps in which
+    // the waves with later tiles finish.  At d = 128 its next two barrier
+    // waits let the 16 stores stay outstanding (`relax` of begin_step), and
+    // the steps after the store are a loop of their own (with the store
+    // inside the one loop the kernel spills); at d <= 64 the 8 stores are
+    // waited for at the next barrier, which measured faster there.
+    constexpr bool kEarlyStore = CAUSAL;
 
     // One pass over the item's key tiles.  The exact pass takes every step
     // through `general` (a row maximum per tile); it runs only if the fast
@@ -758,12 +767,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
         if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
       }
-      for (; t <= ntiles; ++t) {
-        general(t);
-        // After step tw this wave's O and l are final.  A wave whose fast
-        // pass went inexact does not store (its item is redone and every
-        // wave stores again after the exact pass).
-        if (kEarlyStore && !exact && t == tw && !inexact) store_rows();
+      // After step tw this wave's O and l are final.  A wave whose fast
+      // pass went inexact does not store (its item is redone and every wave
+      // stores again after the exact pass).  When it stores before the
+      // item's last step (t = tw < ntiles), all its 32 rows lie before the
+      // sequence end, so it issues all 4 MB store instructions.
+      if constexpr (D > 64) {
+        bool stored = false;
+        for (; t <= ntiles; ++t) {
+          general(t);
+          if (kEarlyStore && !exact && t == tw && !inexact) {
+            store_rows();
+            stored = true;
+            ++t;
+            break;
+          }
+        }
+        for (; t <= ntiles; ++t) general(t, stored && t <= tw + 2);
+      } else {
+        for (; t <= ntiles; ++t) {
+          general(t);
+          if (kEarlyStore && !exact && t == tw && !inexact) store_rows();
+        }
       }
       // No tile load may still be writing this workgroup's LDS when it ends.
       __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
