@@ -33,8 +33,8 @@
 //    the logits, several times the bf16 tolerance at large logits.)
 //  * bf16: K/V tiles go global->LDS by direct loads into a 4-stage ring, and
 //    a persistent grid walks an XCD-aware list of query tiles.  The row sums
-//    of the steady tiles are taken by small MFMAs from the bf16
-//    probabilities, which keeps an add per score off the vector ALU.
+//    are taken by sparse MFMAs from the bf16 probabilities, which keeps an
+//    add per score off the vector ALU.
 //    fp32, key-split: each wave reads its K/V blocks straight from global
 //    memory into MFMA operand registers (no tile is shared between its
 //    waves); fp32, tiles: K/V tiles double-buffered in LDS through
@@ -380,20 +380,35 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // 16 cc + {4h..4h+3, 8+4h..8+4h+3} (the B operand layout of P^T).
     f32x16 sc[2];
     bf16x8 pb[4];
-    // Row sums by MFMA: v_mfma_f32_16x16x32_bf16 with B = a block of P
-    // (lane l's eight values read as column l % 16, contraction slots
-    // 8 (l / 16) .. +7) and this constant A (lane l holds row l % 16 over
-    // the same slots): 1 where the lane's slot group l / 16 equals its
-    // row / 4, else 0.  Output row i then sums the eight B values of lane
-    // group i / 4 in column j, and lane l holds rows 4 (l / 16) .. +3 of
-    // column l % 16: every lane receives, four times, the sum of its own
-    // eight probabilities, in fp32.
-    bf16x8 sum_a;
+    // Row sums by sparse MFMA: v_smfmac_f32_16x16x64_bf16 computes
+    // C[m][n] += sum_k A[m][k] B[k][n] over 64 contraction slots, A stored
+    // 2:4-compressed (in every group of 4 slots, two values and their 2-bit
+    // positions in the index register).  B = two blocks of P (16 values):
+    // lane l holds column l % 16, slots 8 g .. 8 g + 7 and 32 + 8 g .. +7
+    // (g = l / 16); A lane l holds row l % 16 over slots 16 (l / 16) .. +15
+    // (8 stored values, groups of 4 in order, two per group); C lane l holds
+    // rows 4 g .. 4 g + 3 of column l % 16 (layouts measured on gfx950).
+    // The constant A below puts, in rows 4 g and 4 g + 1, ones on exactly
+    // the slots that lane group g of B holds: row 4 g on positions 0 and 1
+    // of each group, row 4 g + 1 on positions 2 and 3 (rows 4 g + 2 and
+    // 4 g + 3 are zero).  C[0] + C[1] of lane l is then the fp32 sum of
+    // the lane's own 16 probabilities; two such products per tile take all
+    // 32, half the matrix-pipe time of the four dense 16x16x32 products
+    // that would take them one block at a time.
+    bf16x8 smf_a;
+    int smf_idx;
     {
-      const bf16_t one = (bf16_t)(((lane >> 4) == ((lane & 15) >> 2)) ? 1.0f : 0.0f);
+      const int m = lane & 15, j = lane >> 4, g = m >> 2, r = m & 3;
+      const bool row_on = r < 2 && (j == (g >> 1) || j == 2 + (g >> 1));
   #pragma unroll
-      for (int e = 0; e < 8; ++e) sum_a[e] = one;
+      for (int e = 0; e < 8; ++e) smf_a[e] = (bf16_t)((row_on && (e >> 2) == (g & 1)) ? 1.0f : 0.0f);
+      const unsigned pat = r == 0 ? 0x4444u : 0xEEEEu;
+      smf_idx = (int)(pat | (pat << 16));
     }
+    auto smf = [&](const bf16x8 &x, const bf16x8 &y, f32x4 c) KB_INLINE {
+      return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+          smf_a, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15), c, smf_idx, 0, 0);
+    };
 
     // Scores of the next tile into sc; each half starts once the
     // probabilities of the old contents (pb[2 half], pb[2 half + 1]) exist.
@@ -466,13 +481,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
     // The lane's share of the row sum l for the current tile: the fp32 sum of
     // its 32 bf16 probabilities, the very weights P V multiplies (so O is
-    // divided by exactly the total of the weights it summed), by the row-sum
-    // MFMAs described at sum_a.  Every tile takes l this way.
+    // divided by exactly the total of the weights it summed), by the sparse
+    // row-sum MFMAs described at smf_a.  Every tile takes l this way.
     auto pb_sum = [&]() KB_INLINE {
-      f32x4 s4 = f32x4{};
-  #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sum_a, pb[cc], s4, 0, 0, 0);
-      return s4[0];
+      f32x4 s4 = smf(pb[0], pb[1], f32x4{});
+      s4 = smf(pb[2], pb[3], s4);
+      return s4[0] + s4[1];
     };
 
     // Steady-state step: O += P(t-1) V(t-1), the softmax of t and S^T(t+1) as
@@ -490,9 +504,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     //               the MFMAs that overwrite it.
     // A steady tile takes no row maximum: its probabilities are taken against
     // the current reference m_run, and the per-lane sum of their bf16 values,
-    // which bounds each of them, is returned.  It is taken by four row-sum
-    // MFMAs, each issued in the slot after its probability block is complete,
-    // so the vector ALU does no add per score.  If some lane's sum exceeds
+    // which bounds each of them, is returned.  It is taken by two sparse
+    // row-sum MFMAs, each issued in the slot after its two probability blocks
+    // are complete, so the vector ALU does no add per score.  If some lane's sum exceeds
     // kSpecLimit (or is not a number below it: a reference stale by more
     // than the fp32 exponential can take gives an infinite probability),
     // the caller corrects the tile or redoes the item exactly.
@@ -573,16 +587,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           sc[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : sc[half]);
         }
         slot_work(i);
-  #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          if (i == sum_slot(cc)) lsv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sum_a, pb[cc], lsv, 0, 0, 0);
+        if (i == sum_slot(1)) lsv = smf(pb[0], pb[1], lsv);
+        if (i == sum_slot(3)) lsv = smf(pb[2], pb[3], lsv);
         // This step's 2 CHW tile loads, spread evenly over the slots so the
         // CU's load pipeline never backs up into the instruction stream.
         constexpr int LDI = NS / (2 * CHW);
         if (i % LDI == 1 % LDI && i / LDI < 2 * CHW) ld(i / LDI);
         __builtin_amdgcn_sched_barrier(0);
       }
-      return lsv[0];
+      return lsv[0] + lsv[1];
     };
 
     // Correction of a steady tile whose sum check failed.  Every probability
@@ -681,10 +694,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                   kst((ST + 2) % kStages), ld);
       float lsum = ls;
       // The check compares bit patterns (the sum is never negative): it also
-      // fails a NaN sum, which the row-sum MFMA gives every lane of a wave in
-      // which some probability is infinite (its zero weights times infinity),
-      // and which a float comparison, compiled here without NaN semantics,
-      // could let through.
+      // fails a NaN sum, which the row-sum MFMA gives the lanes that share a
+      // column with an infinite probability (its zero weights times
+      // infinity), and which a float comparison, compiled here without NaN
+      // semantics, could let through.
       if (__builtin_amdgcn_ballot_w64(__float_as_uint(lsum) > __float_as_uint(kSpecLimit)) != 0 && !spec_fix(lsum))
         inexact = true;
       l_run += lsum;
