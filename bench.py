@@ -376,8 +376,10 @@ def cpu_small_configs(kb, torch, inputs, stream):
 # Datasheet peaks the ceilings are compared with (TFLOP/s; the fp32 vector
 # figure counts packed FMA, which the probe does not use, so its non-packed
 # bound is half of it) and the work per clock per CU of each probe.
-CEIL_PEAK = {"mfma_bf16": 2516.6, "mfma_f32": 157.3, "fma_f32": 157.3 / 2, "exp_f32": None, "mfma_bf16_data": 2516.6}
-CEIL_PER_CLK_CU = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": None, "mfma_bf16_data": 4096}
+CEIL_PEAK = {"mfma_bf16": 2516.6, "mfma_f32": 157.3, "fma_f32": 157.3 / 2, "exp_f32": None, "mfma_bf16_data": 2516.6,
+             "mfma_bf16_fma3": 2516.6, "mfma_bf16_exp3": 2516.6, "mfma_bf16_exp4": 2516.6, "mfma_bf16_lds": 2516.6}
+CEIL_PER_CLK_CU = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": None, "mfma_bf16_data": 4096,
+                   "mfma_bf16_fma3": 4096, "mfma_bf16_exp3": 4096, "mfma_bf16_exp4": 4096, "mfma_bf16_lds": 4096}
 CEIL_MEMORY = ("lds_read", "l1_read", "l2_read")  # read-bandwidth probes, bytes per launch
 
 
@@ -407,6 +409,7 @@ def ceilings(kb, torch, stream, target_ms=40.0):
             row["frac_of_datasheet_peak"] = round(rate / CEIL_PEAK[kind], 4)
         if CEIL_PER_CLK_CU[kind] and mhz > 0:
             row["peak_at_measured_clock"] = round(CEIL_PER_CLK_CU[kind] * cus * mhz * 1e6 / 1e12, 1)
+            row["frac_of_peak_at_measured_clock"] = round(rate / row["peak_at_measured_clock"], 4)
         out[kind] = row
     del work
     return out

@@ -205,9 +205,22 @@ typedef enum {
                             workgroup (vector L1 hits): 1024 bytes each */
   KB_CEIL_L2_READ = 6,   /* the same loads over a 2 MiB region per XCD (L2 hits,
                             L1 misses): 1024 bytes each */
-  KB_CEIL_MFMA_BF16_DATA = 7 /* v_mfma_f32_32x32x16_bf16 on random-bit operands
-                                (8 A and 8 B register sets, a new pair for every
-                                product): 32768 flops each */
+  KB_CEIL_MFMA_BF16_DATA = 7, /* v_mfma_f32_32x32x16_bf16 on random-bit operands
+                                 (8 A and 8 B register sets, a new pair for every
+                                 product): 32768 flops each */
+  /* Co-issue beside the matrix core: v_mfma_f32_32x32x16_bf16 as in
+     KB_CEIL_MFMA_BF16, each product followed by independent work of another
+     kind from the same wave; the rate counts the products' flops only, so
+     it falls below KB_CEIL_MFMA_BF16 once that work no longer fits in the
+     products' shadow (or, for the LDS reads, once their power lowers the
+     clock). */
+  KB_CEIL_MFMA_BF16_FMA3 = 8, /* ... + 3 independent v_fma_f32 per product */
+  KB_CEIL_MFMA_BF16_EXP3 = 9, /* ... + 3 independent v_exp_f32 per product */
+  KB_CEIL_MFMA_BF16_EXP4 = 10, /* ... + 4 independent v_exp_f32 per product */
+  KB_CEIL_MFMA_BF16_LDS = 11  /* ... + one ds_read_b128 after even products and
+                                 two ds_read_b64_tr_b16 after odd ones (the flash
+                                 kernel's LDS mix), each fragment the A operand
+                                 of the product two later */
 } kb_ceiling_kind;
 
 /*

@@ -182,7 +182,8 @@ def test_ceiling_argument_checks():
     ops = ct.c_double()
     clk = ct.c_float()
     # bad kind, iters, reps, warmup, NULL results: rejected before any device query
-    assert lib.kb_bench_ceiling(8, 10, FAKE, 1 << 20, None, 0, 2, per, ct.byref(ops), ct.byref(clk)) == 1
+    bad = max(_lib.CEILINGS.values()) + 1
+    assert lib.kb_bench_ceiling(bad, 10, FAKE, 1 << 20, None, 0, 2, per, ct.byref(ops), ct.byref(clk)) == 1
     assert lib.kb_bench_ceiling(-1, 10, FAKE, 1 << 20, None, 0, 2, per, ct.byref(ops), ct.byref(clk)) == 1
     assert lib.kb_bench_ceiling(0, 0, FAKE, 1 << 20, None, 0, 2, per, ct.byref(ops), ct.byref(clk)) == 1
     assert lib.kb_bench_ceiling(0, 10, FAKE, 1 << 20, None, 0, 0, per, ct.byref(ops), ct.byref(clk)) == 1

@@ -450,7 +450,8 @@ def test_compute_ceiling_probes_run():
     cus = kb.kb_device_info()["compute_units"]
     # per clock per CU (bytes for the memory probes: generous upper bounds)
     bound = {"mfma_bf16": 4096, "mfma_f32": 256, "fma_f32": 128, "exp_f32": 128, "lds_read": 512,
-             "l1_read": 512, "l2_read": 512, "mfma_bf16_data": 4096}
+             "l1_read": 512, "l2_read": 512, "mfma_bf16_data": 4096, "mfma_bf16_fma3": 4096,
+             "mfma_bf16_exp3": 4096, "mfma_bf16_exp4": 4096, "mfma_bf16_lds": 4096}
     for kind in kb.CEILINGS:
         per, ops, mhz = kb.kb_bench_ceiling(kind, 200, work.data_ptr(), work.numel(), 0, 1, 2)
         rate = ops / (min(per) * 1e-3)

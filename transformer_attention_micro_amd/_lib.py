@@ -26,7 +26,8 @@ EXPORTS = ("kb_attention", "kb_attention_naive_noalloc", "kb_attention_workspace
            "kb_bench_triad", "kb_bench_stream", "kb_ceiling_work_size", "kb_bench_ceiling", "kb_device_info",
            "kb_status_string", "kb_last_error")
 CEILINGS = {"mfma_bf16": 0, "mfma_f32": 1, "fma_f32": 2, "exp_f32": 3, "lds_read": 4, "l1_read": 5, "l2_read": 6,
-            "mfma_bf16_data": 7}
+            "mfma_bf16_data": 7, "mfma_bf16_fma3": 8, "mfma_bf16_exp3": 9, "mfma_bf16_exp4": 10,
+            "mfma_bf16_lds": 11}
 STREAMS = {"copy": 1, "read": 2, "write": 3}
 STREAM_BYTES = {"triad": 12, "copy": 8, "read": 4, "write": 4}  # per fp32 element
 

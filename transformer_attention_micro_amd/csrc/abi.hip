@@ -433,7 +433,7 @@ size_t kb_ceiling_work_size(void) {
 kb_status kb_bench_ceiling(int32_t kind, int32_t iters, void *work, size_t work_bytes, void *stream,
                            int32_t warmup, int32_t reps, float *ms_per_rep, double *ops_per_launch,
                            float *clock_mhz) {
-  if (kind < KB_CEIL_MFMA_BF16 || kind > KB_CEIL_MFMA_BF16_DATA) {
+  if (kind < KB_CEIL_MFMA_BF16 || kind > KB_CEIL_MFMA_BF16_LDS) {
     set_err("kind %d is not a kb_ceiling_kind", kind);
     return KB_ERR_INVALID;
   }

@@ -35,6 +35,19 @@
 //                      each product of 8 consecutive iterations, so the
 //                      matrix core switches data like a real product does
 //                      (the other MFMA kind repeats one constant pair)
+//   KB_CEIL_MFMA_BF16_FMA3 / _EXP3 / _EXP4 / _LDS
+//                      co-issue: the constant-operand products of
+//                      KB_CEIL_MFMA_BF16, each followed (in the same wave, in
+//                      a fixed order the compiler may not move) by 3
+//                      independent v_fma_f32, 3 or 4 independent v_exp_f32,
+//                      or LDS reads over the window, one ds_read_b128 after
+//                      even products and a pair of ds_read_b64_tr_b16 after
+//                      odd ones (1.5 per product, the mix of the flash
+//                      step), whose fragment is the A operand of the product
+//                      two later.  The rate counts the
+//                      products only: how much of that other work a wave
+//                      can issue in the products' shadow, two waves per
+//                      SIMD as in the attention kernel, and at what clock.
 // and each wave records the shader clock counter (s_memtime) and the
 // 100 MHz real-time counter (s_memrealtime) around its loop; their ratio is
 // the clock the wave saw.  Every loaded dword feeds an integer sum written
@@ -91,7 +104,7 @@ __global__ __launch_bounds__(kCeilThreads) void ceiling_kernel(int iters, float 
   __shared__ float reserve[96 * 256];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  if constexpr (KIND == KB_CEIL_LDS_READ) {
+  if constexpr (KIND == KB_CEIL_LDS_READ || KIND == KB_CEIL_MFMA_BF16_LDS) {
     // Defined contents for the window the loop reads.
     for (int i = threadIdx.x; i < kLdsWindowChunks * kChunk / 4; i += kCeilThreads) reserve[i] = seed * i;
     __syncthreads();
@@ -145,6 +158,57 @@ __global__ __launch_bounds__(kCeilThreads) void ceiling_kernel(int iters, float 
       if (it + u < iters) step(u);
 #pragma unroll
     for (int c = 0; c < kChains; ++c) r += acc[c][c];
+  } else if constexpr (KIND == KB_CEIL_MFMA_BF16_FMA3 || KIND == KB_CEIL_MFMA_BF16_EXP3 ||
+                       KIND == KB_CEIL_MFMA_BF16_EXP4 || KIND == KB_CEIL_MFMA_BF16_LDS) {
+    constexpr bool kExp = KIND == KB_CEIL_MFMA_BF16_EXP3 || KIND == KB_CEIL_MFMA_BF16_EXP4;
+    constexpr int kV = KIND == KB_CEIL_MFMA_BF16_EXP4 ? 4 : KIND == KB_CEIL_MFMA_BF16_LDS ? 0 : 3;
+    constexpr int kRegs = 16;  // independent vector chains, each touched every 16 / kV products
+    typedef __attribute__((address_space(3))) bf16x8 lds_frag;
+    typedef __attribute__((address_space(3))) s16x4 lds_half;
+    typedef __attribute__((address_space(3))) unsigned char lds_byte;
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (bf16_t)(seed * (lane + i));
+      b[i] = (bf16_t)(seed * (i + 1));
+    }
+    bf16x8 fr[4] = {a, a, a, a};
+    float v[kRegs];
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) v[i] = kExp ? -seed * (lane + i) : seed * (lane + i);
+    const float m = 1.0f - 1e-7f * seed, s = 1e-7f;
+    const lds_byte *win = (const lds_byte *)(const __attribute__((address_space(3))) float *)reserve + lane * 16;
+    f32x16 acc[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) {
+        acc[c] = mfma32x16_bf16(KIND == KB_CEIL_MFMA_BF16_LDS ? fr[c & 3] : a, b, acc[c]);
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+          float &x = v[(c * kV + k) % kRegs];
+          x = kExp ? exp2_fast(x) : fmaf(x, m, s);
+        }
+        if constexpr (KIND == KB_CEIL_MFMA_BF16_LDS) {
+          // Even products: one 16-byte read of 1 KiB chunk (it * 8 + c) mod
+          // 32 of the window; odd ones: two 8-byte transposing reads of it.
+          const lds_byte *p = win + (((unsigned)(it * kChains + c)) & 31u) * kChunk;
+          if ((c & 1) == 0) {
+            fr[(c + 2) & 3] = *(const lds_frag *)p;
+          } else {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_half *)p);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_half *)(p + 512));
+            fr[(c + 2) & 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) r += acc[c][c];
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) r += v[i];
   } else if constexpr (KIND == KB_CEIL_MFMA_F32) {
     const float a = seed * lane, b = seed;
     f32x16 acc[kChains];
@@ -227,7 +291,10 @@ void launch_kind(int cus, int iters, unsigned long long *clk, float *sink, const
 int kb_ceiling_waves(int cus) { return cus * kCeilWaves; }
 
 double kb_ceiling_ops(int kind, int cus, int iters) {
-  const double per_instr = kind == KB_CEIL_MFMA_BF16 || kind == KB_CEIL_MFMA_BF16_DATA ? 2.0 * 32 * 32 * 16
+  const bool bf16_mfma = kind == KB_CEIL_MFMA_BF16 || kind == KB_CEIL_MFMA_BF16_DATA || kind == KB_CEIL_MFMA_BF16_FMA3 ||
+                         kind == KB_CEIL_MFMA_BF16_EXP3 || kind == KB_CEIL_MFMA_BF16_EXP4 ||
+                         kind == KB_CEIL_MFMA_BF16_LDS;
+  const double per_instr = bf16_mfma ? 2.0 * 32 * 32 * 16
                            : kind == KB_CEIL_MFMA_F32 ? 2.0 * 32 * 32 * 2
                            : kind == KB_CEIL_FMA_F32  ? 2.0 * kWave
                            : kind == KB_CEIL_EXP_F32  ? 1.0 * kWave
@@ -259,6 +326,18 @@ hipError_t kb_launch_ceiling(int kind, int cus, int iters, unsigned long long *c
     case KB_CEIL_L2_READ: launch_kind<KB_CEIL_L2_READ>(cus, iters, clk, sink, data, stream); break;
     case KB_CEIL_MFMA_BF16_DATA:
       launch_kind<KB_CEIL_MFMA_BF16_DATA>(cus, iters, clk, sink, data, stream);
+      break;
+    case KB_CEIL_MFMA_BF16_FMA3:
+      launch_kind<KB_CEIL_MFMA_BF16_FMA3>(cus, iters, clk, sink, data, stream);
+      break;
+    case KB_CEIL_MFMA_BF16_EXP3:
+      launch_kind<KB_CEIL_MFMA_BF16_EXP3>(cus, iters, clk, sink, data, stream);
+      break;
+    case KB_CEIL_MFMA_BF16_EXP4:
+      launch_kind<KB_CEIL_MFMA_BF16_EXP4>(cus, iters, clk, sink, data, stream);
+      break;
+    case KB_CEIL_MFMA_BF16_LDS:
+      launch_kind<KB_CEIL_MFMA_BF16_LDS>(cus, iters, clk, sink, data, stream);
       break;
     default: return hipErrorInvalidValue;
   }
