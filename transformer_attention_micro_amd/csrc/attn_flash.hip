@@ -300,7 +300,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
     auto dma = [&](bool is_v, int i, lds_bf16 *dst, uint32_t toff) KB_INLINE {
-      if (w + NW * i >= NI) return;
+      // Wave w issues instruction w + NW i of the tile; when NI = NW CHW
+      // (d >= 64) every wave issues all CHW of them, known at compile time,
+      // so the loads of a step carry no branch.
+      if (NI < NW * CHW && w + NW * i >= NI) return;
       const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + (w + NW * i) * 512));
       if (is_v)
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
