@@ -436,12 +436,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     auto mask = [&](int t) KB_INLINE {
       const int kt0 = t * BC;
       if ((kt0 + BC > S) || (CAUSAL && kt0 + BC - 1 > qw)) {
-        const int lim = (CAUSAL ? min(q, S - 1) : S - 1) - kt0;
+        // Key 32 sb + acc_row(v, h) is c(sb, v) + 4 h, c a constant of 0..63:
+        // one per-lane limit, and each score a compare with an inline
+        // constant and a select, both through VCC (written out, because the
+        // compiler otherwise keeps all 32 compare results, or 32 per-lane
+        // key offsets, live across the kernel and spills registers).
+        const int lim = (CAUSAL ? min(q, S - 1) : S - 1) - kt0 - 4 * h;
+        const float ninf = -INFINITY;
   #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
   #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (32 * sb + acc_row(v, h) > lim) sc[sb][v] = -INFINITY;
+          for (int v = 0; v < 16; ++v) {
+            float x = sc[sb][v];
+            asm volatile("v_cmp_lt_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
+                         : "+v"(x) : "v"(lim), "i"(32 * sb + 8 * (v >> 2) + (v & 3)), "v"(ninf) : "vcc");
+            sc[sb][v] = x;
+          }
       }
     };
     // Softmax, first part: row max and lazy rescaling.  The row max is taken
