@@ -40,8 +40,9 @@
 //    waves); fp32, tiles: K/V tiles double-buffered in LDS through
 //    registers.  Both on a dispatched grid.
 //  * O and l share a reference m that need not be the running maximum (O / l
-//    does not depend on it in exact arithmetic).  bf16: the first, diagonal,
-//    ragged and last tiles take the exact row maximum; the others take none
+//    does not depend on it in exact arithmetic).  bf16: the first tile
+//    (and, non-causal, the last) takes the exact row maximum; the others
+//    (a causal wave's diagonal tile among them, masked first) take none
 //    and check the sum of their probabilities instead, correcting the tile
 //    in place (or, if the exponentials overflowed, recomputing the query
 //    tile exactly) when the reference proves stale.
@@ -162,8 +163,8 @@ __device__ __forceinline__ void pin(T &x) {
 // work:
 //   O^T += V(t-1)^T P(t-1)^T    (MFMA, V from LDS, P from registers)
 //   softmax of tile t           (vector ALU: exponentials, bf16 P; a row
-//                                max only on the first, diagonal and last
-//                                tiles)
+//                                max only on the first tile and, non-causal,
+//                                the last)
 //   S^T(t+1) = K(t+1) Q^T       (MFMA, K from LDS)
 // and its instruction stream interleaves them, so the vector ALU works in
 // the shadow of the matrix core (a wave keeps issuing independent
@@ -715,6 +716,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         inexact = true;
       l_run += lsum;
     };
+    // Causal: the wave's last tile (its diagonal one) as a fused step, the
+    // same instruction stream as a steady step but with its ring stages
+    // chosen at run time and the mask applied first; its probabilities are
+    // checked by their sum like a steady tile's (every row has a visible key
+    // there).  Its score MFMAs for tile tw read a tile no one uses (or the
+    // zero-filled stage past the end).  A general step here took twice as
+    // long, and every wave of the workgroup waited for it at the next
+    // barrier.
+    auto steady_last = [&](int t) KB_INLINE {
+      const int st = t & 3;
+      begin_step(t);
+      mask(t);
+      const uint32_t tk = tile_off(t + 4), tv = tile_off(t + 2);
+      auto ld = [&](int k) KB_INLINE {
+        if (k < CHW) dma(false, k, kst(st), tk);
+        else dma(true, k - CHW, vst((st + 2) & 3), tv);
+      };
+      float lsum = fused_step(vst((st + 3) & 3), kst((st + 1) & 3), vst(st), kst((st + 2) & 3), ld);
+      if (__builtin_amdgcn_ballot_w64(__float_as_uint(lsum) > __float_as_uint(kSpecLimit)) != 0 && !spec_fix(lsum))
+        inexact = true;
+      l_run += lsum;
+    };
     // Any step, buffers chosen at run time: the first, the last two of the
     // wave and the idle steps of causal waves that finished early (each wave
     // takes part in every step's barrier and loads).
@@ -779,7 +802,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       general(0);
       int t = 1;
       if (!exact) {
-        // Steady steps 1 .. tw - 2: four per iteration, then up to three more.
+        // Steady steps 1 .. tw - 2: four per iteration, then up to three more;
+        // then, causal, the wave's last tile.
         // The first fragments of step 1 are V(0) (stage 0), read ahead here.
   #pragma unroll
         for (int i = 0; i < kPre; ++i) buf[i] = fetch_first(vst(0), kst(2), i);
@@ -792,12 +816,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (t <= tw - 2) steady(std::integral_constant<int, 1>{}, t++);
         if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
         if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
+        if (CAUSAL && t == tw - 1) steady_last(t++);
       }
       // After step tw this wave's O and l are final.  A wave whose fast
       // pass went inexact does not store (its item is redone and every wave
       // stores again after the exact pass).  When it stores before the
       // item's last step (t = tw < ntiles), all its 32 rows lie before the
       // sequence end, so it issues all 4 MB store instructions.
+      // A store in the item's last step leaves the 4 MB store instructions
+      // as the youngest memory operations (if the wave has a row before the
+      // sequence end, all of them issue).
+      bool last_store = false;
       if constexpr (D > 64) {
         bool stored = false;
         for (; t <= ntiles; ++t) {
@@ -805,6 +834,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           if (kEarlyStore && !exact && t == tw && !inexact) {
             store_rows();
             stored = true;
+            last_store = t == ntiles && qw < S;
             ++t;
             break;
           }
@@ -813,11 +843,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       } else {
         for (; t <= ntiles; ++t) {
           general(t);
-          if (kEarlyStore && !exact && t == tw && !inexact) store_rows();
+          if (kEarlyStore && !exact && t == tw && !inexact) {
+            store_rows();
+            last_store = t == ntiles && qw < S;
+          }
         }
       }
-      // No tile load may still be writing this workgroup's LDS when it ends.
-      __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
+      // No tile load may still be writing this workgroup's LDS when it ends
+      // (vmcnt retires in issue order: past the stores of the last step, the
+      // loads are in; the next item's prologue waits for the stores).
+      if (last_store)
+        __builtin_amdgcn_s_waitcnt(wait_vm_imm(4 * MB));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
     };
 
     // Cleared before the prologue's barrier; set by any wave whose fast pass
