@@ -168,11 +168,14 @@ __device__ __forceinline__ void pin(T &x) {
 //   S^T(t+1) = K(t+1) Q^T       (MFMA, K from LDS)
 // and its instruction stream interleaves them, so the vector ALU works in
 // the shadow of the matrix core (a wave keeps issuing independent
-// instructions while an MFMA runs).  Scores and probabilities live in one
-// set of registers: the MFMAs of P(t-1) V(t-1) read each P block before the
+// instructions while an MFMA runs).  At d = 128 scores live in one set of
+// registers: the MFMAs of P(t-1) V(t-1) read each P block before the
 // softmax overwrites it, and the score MFMAs of each 32-key half of t+1
-// start once the softmax has consumed that half.  When the softmax of t
-// moves the reference maximum, O is rescaled after P(t-1) V(t-1) is in.
+// start once the softmax has consumed that half.  At d <= 64, where a step
+// has half the products for the same vector work, consecutive tiles' scores
+// alternate between two register sets and the softmax spreads over the
+// whole step.  When the softmax of t moves the reference maximum, O is
+// rescaled after P(t-1) V(t-1) is in.
 //
 // LDS: rings of kStages K tiles and kStages V tiles filled by direct
 // global->LDS loads; step t issues K(t+4) and V(t+2), and waits (before its
@@ -382,7 +385,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // of half sb (raw dot products).  Probabilities in bf16: pb[cc] =
     // accumulator slots 8(cc & 1) .. +7 of half cc / 2, i.e. keys
     // 16 cc + {4h..4h+3, 8+4h..8+4h+3} (the B operand layout of P^T).
-    f32x16 sc[2];
+    // At d <= 64 the steady steps keep the scores of consecutive tiles in
+    // two register sets (tile t in scd[t & 1]; sc is scd[1], the set every
+    // other step uses), so the softmax of tile t and the score products of
+    // tile t + 1 need not take turns.
+    f32x16 scd[2][2];
+    f32x16(&sc)[2] = scd[1];
     bf16x8 pb[4];
     // Row sums by sparse MFMA: v_smfmac_f32_16x16x64_bf16 computes
     // C[m][n] += sum_k A[m][k] B[k][n] over 64 contraction slots, A stored
@@ -528,13 +536,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // conversion of each pair trails one op behind, so no vector instruction
     // waits on the one just before it.
     auto fused_step = [&](const lds_bf16 *vprev, const lds_bf16 *knext, const lds_bf16 *vnn,
-                          const lds_bf16 *knn, auto &&ld) KB_INLINE {
+                          const lds_bf16 *knn, auto &&ld, auto next_tag) KB_INLINE {
+      constexpr bool NEXT = decltype(next_tag)::value;
       constexpr int NS = NPV + 2 * KC;
       constexpr int A0 = NPV / 4, B0 = 3 * NPV / 4, E1 = NPV + KC;
       static_assert(NS % kPre == 0 && NPV >= kPre, "fragment ring");
       // Fragment i of this step (i < NS) or of the next one (i >= NS, read
       // from the next step's stages, resident since this step's barrier).
+      // Without NEXT (a wave's last tile) the scores of the next tile and
+      // the next step's fragments are not needed and not read.
       auto fetch = [&](int i) KB_INLINE {
+        if (!NEXT && i >= NPV) return bf16x8{};
         if (i >= NS) return fetch_first(vnn, knn, i - NS);
         return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
       };
@@ -596,7 +608,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         buf[i % kPre] = fetch(i + kPre);
         if (i < NPV) {
           oacc[i % MB] = mfma32x16_bf16(op, pbo[i / MB], oacc[i % MB]);
-        } else {
+        } else if constexpr (NEXT) {
           const int half = (i - NPV) / KC, kc = (i - NPV) % KC;
           sc[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : sc[half]);
         }
@@ -605,6 +617,84 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (i == sum_slot(3)) lsv = smf(pb[2], pb[3], lsv);
         // This step's 2 CHW tile loads, spread evenly over the slots so the
         // CU's load pipeline never backs up into the instruction stream.
+        constexpr int LDI = NS / (2 * CHW);
+        if (i % LDI == 1 % LDI && i / LDI < 2 * CHW) ld(i / LDI);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return lsv[0] + lsv[1];
+    };
+
+    // d <= 64: the same step with the scores of tile t in `cur` and those of
+    // tile t + 1 written to `nxt`.  The softmax of t no longer has to finish
+    // before the score products of t + 1 start, so its 18 exponential ops
+    // are dealt evenly over all NS slots (with one set they fit between the
+    // P V products that read each old probability block and the score
+    // products that overwrite each half, leaving slots with no vector work,
+    // where the step is bound by the vector ALU).
+    auto fused_step_db = [&](const lds_bf16 *vprev, const lds_bf16 *knext, const lds_bf16 *vnn,
+                             const lds_bf16 *knn, auto &&ld, auto next_tag, f32x16(&cur)[2],
+                             f32x16(&nxt)[2]) KB_INLINE {
+      constexpr bool NEXT = decltype(next_tag)::value;
+      constexpr int NS = NPV + 2 * KC;
+      constexpr int NOP = 18;
+      static_assert(NS % kPre == 0 && NPV >= kPre, "fragment ring");
+      auto fetch = [&](int i) KB_INLINE {
+        if (!NEXT && i >= NPV) return bf16x8{};
+        if (i >= NS) return fetch_first(vnn, knn, i - NS);
+        return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
+      };
+      const float nm = -m_run;
+      f32x4 lsv = f32x4{};
+      auto cvt_pair = [&](int sb, int p) KB_INLINE {
+        bf16x2 pr = {(bf16_t)cur[sb][2 * p], (bf16_t)cur[sb][2 * p + 1]};
+        pin(pr);
+        const int cc = 2 * sb + p / 4, e = p % 4;
+        pb[cc][2 * e] = pr[0];
+        pb[cc][2 * e + 1] = pr[1];
+      };
+      // Op k (0..17) is op k % 9 of half k / 9: the exponentials of pair
+      // k % 9 (if below 8), then the conversion of the pair before it.
+      auto exp_op = [&](int k) KB_INLINE {
+        const int sb = k / 9, p = k % 9;
+        if (p < 8) {
+          float x0 = cur[sb][2 * p], x1 = cur[sb][2 * p + 1];
+          pin(x0);
+          pin(x1);
+          x0 = fmaf(x0, sl2e, nm);
+          x1 = fmaf(x1, sl2e, nm);
+          x0 = exp2_fast(x0);
+          x1 = exp2_fast(x1);
+          pin(x0);
+          pin(x1);
+          cur[sb][2 * p] = x0;
+          cur[sb][2 * p + 1] = x1;
+        }
+        if (p > 0) cvt_pair(sb, p - 1);
+      };
+      // Slot i runs ops [NOP i / NS, NOP (i + 1) / NS); the row sum of blocks
+      // 0 and 1 follows the slot of op 8, that of blocks 2 and 3 the last.
+      constexpr auto op_slot = [](int k) {
+        for (int i = 0; i < NS; ++i)
+          if ((NOP * i) / NS <= k && k < (NOP * (i + 1)) / NS) return i;
+        return -1;
+      };
+      static_assert(op_slot(NOP - 1) == NS - 1, "ops dealt over every slot");
+      bf16x8 pbo[4];
+  #pragma unroll
+      for (int cc = 0; cc < 4; ++cc) pbo[cc] = pb[cc];
+  #pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const bf16x8 op = buf[i % kPre];
+        buf[i % kPre] = fetch(i + kPre);
+        if (i < NPV) {
+          oacc[i % MB] = mfma32x16_bf16(op, pbo[i / MB], oacc[i % MB]);
+        } else if constexpr (NEXT) {
+          const int half = (i - NPV) / KC, kc = (i - NPV) % KC;
+          nxt[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : nxt[half]);
+        }
+        for (int k = (NOP * i) / NS; k < (NOP * (i + 1)) / NS; ++k) exp_op(k);
+        if (i == op_slot(8)) lsv = smf(pb[0], pb[1], lsv);
+        if (i == NS - 1) lsv = smf(pb[2], pb[3], lsv);
         constexpr int LDI = NS / (2 * CHW);
         if (i % LDI == 1 % LDI && i / LDI < 2 * CHW) ld(i / LDI);
         __builtin_amdgcn_sched_barrier(0);
@@ -675,13 +765,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // t % 4) and V(t-2) (stage (t + 2) % 4), which are refilled with K(t+4)
     // and V(t+2); K(t+2) and V(t) are now readable, so the end of step t
     // reads the first fragments of step t+1 from them.
+    // `drain` (the steps after a general one, or after the prologue): wait
+    // for every LDS read, since the score products that end such a step read
+    // the K stage that step t refills.
     // `relax`: the wave issued its 4 MB output stores at the end of step
     // t-1 or t-2, after the loads this wait is for.  vmcnt counts loads and
     // stores together and retires them in issue order, so allowing those
     // stores to stay outstanding still leaves the wanted loads complete.
-    auto begin_step = [&](int t, bool relax = false) KB_INLINE {
-      if (relax)
+    auto begin_step = [&](int t, bool relax = false, bool drain = false) KB_INLINE {
+      if (relax && drain)
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm_imm(2 * CHW + 4 * MB, 0));
+      else if (relax)
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm_imm(2 * CHW + 4 * MB, 2 * kPre));
+      else if (drain)
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm_imm(2 * CHW, 0));
       else
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm_imm(2 * CHW, 2 * kPre));
       asm volatile("" ::: "memory");
@@ -704,8 +801,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (k < CHW) dma(false, k, kst(ST), tk);
         else dma(true, k - CHW, vst((ST + 2) % kStages), tv);
       };
-      const float ls = fused_step(vst((ST + 3) % kStages), kst((ST + 1) % kStages), vst(ST),
-                                  kst((ST + 2) % kStages), ld);
+      float ls;
+      if constexpr (D <= 64)
+        ls = fused_step_db(vst((ST + 3) % kStages), kst((ST + 1) % kStages), vst(ST), kst((ST + 2) % kStages), ld,
+                           std::true_type{}, scd[ST & 1], scd[(ST + 1) & 1]);
+      else
+        ls = fused_step(vst((ST + 3) % kStages), kst((ST + 1) % kStages), vst(ST), kst((ST + 2) % kStages), ld,
+                        std::true_type{});
       float lsum = ls;
       // The check compares bit patterns (the sum is never negative): it also
       // fails a NaN sum, which the row-sum MFMA gives the lanes that share a
@@ -718,12 +820,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
     // Causal: the wave's last tile (its diagonal one) as a fused step, the
     // same instruction stream as a steady step but with its ring stages
-    // chosen at run time and the mask applied first; its probabilities are
-    // checked by their sum like a steady tile's (every row has a visible key
-    // there).  Its score MFMAs for tile tw read a tile no one uses (or the
-    // zero-filled stage past the end).  A general step here took twice as
-    // long, and every wave of the workgroup waited for it at the next
-    // barrier.
+    // chosen at run time, the mask applied first and no score products for a
+    // next tile; its probabilities are checked by their sum like a steady
+    // tile's (every row has a visible key there).  A general step here took
+    // twice as long, and every wave of the workgroup waited for it at the
+    // next barrier.
     auto steady_last = [&](int t) KB_INLINE {
       const int st = t & 3;
       begin_step(t);
@@ -733,7 +834,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (k < CHW) dma(false, k, kst(st), tk);
         else dma(true, k - CHW, vst((st + 2) & 3), tv);
       };
-      float lsum = fused_step(vst((st + 3) & 3), kst((st + 1) & 3), vst(st), kst((st + 2) & 3), ld);
+      float lsum;
+      if constexpr (D <= 64)
+        lsum = fused_step_db(vst((st + 3) & 3), kst((st + 1) & 3), vst(st), kst((st + 2) & 3), ld, std::false_type{},
+                             scd[1], scd[0]);
+      else
+        lsum = fused_step(vst((st + 3) & 3), kst((st + 1) & 3), vst(st), kst((st + 2) & 3), ld, std::false_type{});
       if (__builtin_amdgcn_ballot_w64(__float_as_uint(lsum) > __float_as_uint(kSpecLimit)) != 0 && !spec_fix(lsum))
         inexact = true;
       l_run += lsum;
@@ -743,7 +849,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // takes part in every step's barrier and loads).
     auto general = [&](int t, bool relax = false) KB_INLINE {
       const int st = t & 3;
-      begin_step(t, relax);
+      begin_step(t, relax, true);
       load_tile(false, kst(st), t + 4);
       load_tile(true, vst((st + 2) & 3), t + 2);
       float alpha = 1.f;
@@ -816,6 +922,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (t <= tw - 2) steady(std::integral_constant<int, 1>{}, t++);
         if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
         if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
+        // The scores of tile t are in scd[t & 1]; the steps that follow read sc.
+        if constexpr (D <= 64) {
+          if ((t & 1) == 0) {
+            scd[1][0] = scd[0][0];
+            scd[1][1] = scd[0][1];
+          }
+        }
         if (CAUSAL && t == tw - 1) steady_last(t++);
       }
       // After step tw this wave's O and l are final.  A wave whose fast
