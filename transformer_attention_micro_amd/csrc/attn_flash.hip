@@ -253,6 +253,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
     bool inexact = false;  // a steady tile's reference was stale beyond repair
+    int pv_lim = 0;        // tiles whose P V the general steps still do
 
     const int kend = CAUSAL ? min(S, q0 + BR) : S;
     const int ntiles = (kend + BC - 1) / BC;
@@ -385,9 +386,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // of half sb (raw dot products).  Probabilities in bf16: pb[cc] =
     // accumulator slots 8(cc & 1) .. +7 of half cc / 2, i.e. keys
     // 16 cc + {4h..4h+3, 8+4h..8+4h+3} (the B operand layout of P^T).
-    // At d <= 64 the steady steps keep the scores of consecutive tiles in
-    // two register sets (tile t in scd[t & 1]; sc is scd[1], the set every
-    // other step uses), so the softmax of tile t and the score products of
+    // At d <= 64 the fused steps keep the scores of consecutive tiles in two
+    // register sets (tile t in scd[(t + 1) & 1]; sc is scd[1], the set the
+    // other steps use), so the softmax of tile t and the score products of
     // tile t + 1 need not take turns.
     f32x16 scd[2][2];
     f32x16(&sc)[2] = scd[1];
@@ -536,8 +537,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // conversion of each pair trails one op behind, so no vector instruction
     // waits on the one just before it.
     auto fused_step = [&](const lds_bf16 *vprev, const lds_bf16 *knext, const lds_bf16 *vnn,
-                          const lds_bf16 *knn, auto &&ld, auto next_tag) KB_INLINE {
-      constexpr bool NEXT = decltype(next_tag)::value;
+                          const lds_bf16 *knn, auto &&ld, auto prev_tag, auto next_tag) KB_INLINE {
+      constexpr bool PREV = decltype(prev_tag)::value, NEXT = decltype(next_tag)::value;
       constexpr int NS = NPV + 2 * KC;
       constexpr int A0 = NPV / 4, B0 = 3 * NPV / 4, E1 = NPV + KC;
       static_assert(NS % kPre == 0 && NPV >= kPre, "fragment ring");
@@ -547,6 +548,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // the next step's fragments are not needed and not read.
       auto fetch = [&](int i) KB_INLINE {
         if (!NEXT && i >= NPV) return bf16x8{};
+        if (!PREV && i < NPV) return bf16x8{};
         if (i >= NS) return fetch_first(vnn, knn, i - NS);
         return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
       };
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const bf16x8 op = buf[i % kPre];
         buf[i % kPre] = fetch(i + kPre);
         if (i < NPV) {
-          oacc[i % MB] = mfma32x16_bf16(op, pbo[i / MB], oacc[i % MB]);
+          if constexpr (PREV) oacc[i % MB] = mfma32x16_bf16(op, pbo[i / MB], oacc[i % MB]);
         } else if constexpr (NEXT) {
           const int half = (i - NPV) / KC, kc = (i - NPV) % KC;
           sc[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : sc[half]);
@@ -632,14 +634,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // products that overwrite each half, leaving slots with no vector work,
     // where the step is bound by the vector ALU).
     auto fused_step_db = [&](const lds_bf16 *vprev, const lds_bf16 *knext, const lds_bf16 *vnn,
-                             const lds_bf16 *knn, auto &&ld, auto next_tag, f32x16(&cur)[2],
+                             const lds_bf16 *knn, auto &&ld, auto prev_tag, auto next_tag, f32x16(&cur)[2],
                              f32x16(&nxt)[2]) KB_INLINE {
-      constexpr bool NEXT = decltype(next_tag)::value;
+      constexpr bool PREV = decltype(prev_tag)::value, NEXT = decltype(next_tag)::value;
       constexpr int NS = NPV + 2 * KC;
       constexpr int NOP = 18;
       static_assert(NS % kPre == 0 && NPV >= kPre, "fragment ring");
       auto fetch = [&](int i) KB_INLINE {
         if (!NEXT && i >= NPV) return bf16x8{};
+        if (!PREV && i < NPV) return bf16x8{};
         if (i >= NS) return fetch_first(vnn, knn, i - NS);
         return i < NPV ? vfrag(vprev, i) : kfrag(knext, (i - NPV) / KC, (i - NPV) % KC);
       };
@@ -687,7 +690,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const bf16x8 op = buf[i % kPre];
         buf[i % kPre] = fetch(i + kPre);
         if (i < NPV) {
-          oacc[i % MB] = mfma32x16_bf16(op, pbo[i / MB], oacc[i % MB]);
+          if constexpr (PREV) oacc[i % MB] = mfma32x16_bf16(op, pbo[i / MB], oacc[i % MB]);
         } else if constexpr (NEXT) {
           const int half = (i - NPV) / KC, kc = (i - NPV) % KC;
           nxt[half] = mfma32x16_bf16(op, qf[kc], kc == 0 ? f32x16{} : nxt[half]);
@@ -804,10 +807,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       float ls;
       if constexpr (D <= 64)
         ls = fused_step_db(vst((ST + 3) % kStages), kst((ST + 1) % kStages), vst(ST), kst((ST + 2) % kStages), ld,
-                           std::true_type{}, scd[ST & 1], scd[(ST + 1) & 1]);
+                           std::true_type{}, std::true_type{}, scd[(ST + 1) & 1], scd[ST & 1]);
       else
         ls = fused_step(vst((ST + 3) % kStages), kst((ST + 1) % kStages), vst(ST), kst((ST + 2) % kStages), ld,
-                        std::true_type{});
+                        std::true_type{}, std::true_type{});
       float lsum = ls;
       // The check compares bit patterns (the sum is never negative): it also
       // fails a NaN sum, which the row-sum MFMA gives the lanes that share a
@@ -836,10 +839,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       };
       float lsum;
       if constexpr (D <= 64)
-        lsum = fused_step_db(vst((st + 3) & 3), kst((st + 1) & 3), vst(st), kst((st + 2) & 3), ld, std::false_type{},
-                             scd[1], scd[0]);
+        lsum = fused_step_db(vst((st + 3) & 3), kst((st + 1) & 3), vst(st), kst((st + 2) & 3), ld, std::true_type{},
+                             std::false_type{}, scd[1], scd[0]);
       else
-        lsum = fused_step(vst((st + 3) & 3), kst((st + 1) & 3), vst(st), kst((st + 2) & 3), ld, std::false_type{});
+        lsum = fused_step(vst((st + 3) & 3), kst((st + 1) & 3), vst(st), kst((st + 2) & 3), ld, std::true_type{},
+                          std::false_type{});
       if (__builtin_amdgcn_ballot_w64(__float_as_uint(lsum) > __float_as_uint(kSpecLimit)) != 0 && !spec_fix(lsum))
         inexact = true;
       l_run += lsum;
@@ -854,7 +858,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       load_tile(true, vst((st + 2) & 3), t + 2);
       float alpha = 1.f;
       bool grow = false;
-      if (t >= 1 && t - 1 < tw) pv(vst((st + 3) & 3));
+      if (t >= 1 && t - 1 < pv_lim) pv(vst((st + 3) & 3));
       if (t < tw) {
         mask(t);
         grow = row_max(alpha, kRescaleLog2);
@@ -890,10 +894,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // waited for at the next barrier, which measured faster there.
     constexpr bool kEarlyStore = CAUSAL;
 
+    // Fast pass, step 0: the exact row maximum of tile 0 (the reference for
+    // the steady tiles), then the softmax of tile 0 interleaved with the
+    // score products of tile 1 in the fused instruction stream (no P V yet).
+    // The prologue's score products read stage 0, which this step refills.
+    auto step0 = [&]() KB_INLINE {
+      begin_step(0, false, true);
+      mask(0);
+      float alpha;
+      row_max(alpha, 0.f);
+      const uint32_t tk = tile_off(4), tv = tile_off(2);
+      auto ld = [&](int k) KB_INLINE {
+        if (k < CHW) dma(false, k, kst(0), tk);
+        else dma(true, k - CHW, vst(2), tv);
+      };
+      float lsum;
+      if constexpr (D <= 64)
+        lsum = fused_step_db(vst(3), kst(1), vst(0), kst(2), ld, std::false_type{}, std::true_type{}, scd[1], scd[0]);
+      else
+        lsum = fused_step(vst(3), kst(1), vst(0), kst(2), ld, std::false_type{}, std::true_type{});
+      l_run += lsum;
+    };
+
     // One pass over the item's key tiles.  The exact pass takes every step
     // through `general` (a row maximum per tile); it runs only if the fast
     // pass met a tile whose reference was stale beyond repair.
     auto pass = [&](bool exact) KB_INLINE {
+      pv_lim = tw;
+      int st_step = -8;  // step at whose end this wave issued its output stores
       // Prologue: K(0..3), V(0..1); every wave computes S^T(0).
       load_tile(false, kst(0), 0);
       load_tile(false, kst(1), 1);
@@ -905,14 +933,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       wg_barrier();
       qk(kst(0));
 
-      general(0);
+      if (exact)
+        general(0);
+      else
+        step0();
       int t = 1;
       if (!exact) {
         // Steady steps 1 .. tw - 2: four per iteration, then up to three more;
-        // then, causal, the wave's last tile.
-        // The first fragments of step 1 are V(0) (stage 0), read ahead here.
-  #pragma unroll
-        for (int i = 0; i < kPre; ++i) buf[i] = fetch_first(vst(0), kst(2), i);
+        // then, causal, the wave's last tile.  (Step 0 read the first
+        // fragments of step 1, V(0), ahead.)
         for (; t + 3 <= tw - 2; t += 4) {
           steady(std::integral_constant<int, 1>{}, t);
           steady(std::integral_constant<int, 2>{}, t + 1);
@@ -922,46 +951,71 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (t <= tw - 2) steady(std::integral_constant<int, 1>{}, t++);
         if (t <= tw - 2) steady(std::integral_constant<int, 2>{}, t++);
         if (t <= tw - 2) steady(std::integral_constant<int, 3>{}, t++);
-        // The scores of tile t are in scd[t & 1]; the steps that follow read sc.
+        // The scores of tile t are in scd[(t + 1) & 1]; the steps that follow
+        // read sc.
         if constexpr (D <= 64) {
-          if ((t & 1) == 0) {
+          if ((t & 1) == 1) {
             scd[1][0] = scd[0][0];
             scd[1][1] = scd[0][1];
           }
         }
-        if (CAUSAL && t == tw - 1) steady_last(t++);
+        // A causal wave's last tile.  The item's last waves then take its
+        // P V right away (V(t) is resident: every wave waited for it at this
+        // step's barrier) and store their rows, so the item needs no step
+        // after it.  (Earlier waves leave that P V to the next step, which
+        // the others spend on steady work anyway: done here it held up the
+        // next barrier.)
+        if (CAUSAL && t == tw - 1) {
+          steady_last(t);
+          if (tw == ntiles) {
+            pv(vst(t & 3));
+            pv_lim = tw - 1;
+            if (!inexact) {
+              store_rows();
+              st_step = t;
+            }
+          }
+          ++t;
+        }
       }
-      // After step tw this wave's O and l are final.  A wave whose fast
-      // pass went inexact does not store (its item is redone and every wave
-      // stores again after the exact pass).  When it stores before the
-      // item's last step (t = tw < ntiles), all its 32 rows lie before the
-      // sequence end, so it issues all 4 MB store instructions.
+      // Once the P V of its last tile is in, a wave's O and l are final and
+      // it stores its rows: the item's last waves (tw = ntiles) in the step
+      // of their last tile, the others after the general step that takes
+      // that P V (all their 32 rows then lie before the sequence end, so
+      // they issue all 4 MB store instructions).  A wave whose fast pass
+      // went inexact does not store (its item is redone and every wave
+      // stores after the exact pass).  The fast causal pass ends with the
+      // step of the last waves' last tile; otherwise a final step takes the
+      // P V of every wave's last tile.
+      const int last = (CAUSAL && !exact && ntiles >= 2) ? ntiles - 1 : ntiles;
+      if constexpr (D > 64) {
+        bool stored = st_step >= 0;
+        if (!stored) {
+          for (; t <= last; ++t) {
+            general(t);
+            if (kEarlyStore && !exact && t == tw && !inexact) {
+              store_rows();
+              stored = true;
+              st_step = t;
+              ++t;
+              break;
+            }
+          }
+        }
+        for (; t <= last; ++t) general(t, stored && t <= st_step + 2);
+      } else {
+        for (; t <= last; ++t) {
+          general(t);
+          if (kEarlyStore && !exact && t == tw && st_step < 0 && !inexact) {
+            store_rows();
+            st_step = t;
+          }
+        }
+      }
       // A store in the item's last step leaves the 4 MB store instructions
       // as the youngest memory operations (if the wave has a row before the
       // sequence end, all of them issue).
-      bool last_store = false;
-      if constexpr (D > 64) {
-        bool stored = false;
-        for (; t <= ntiles; ++t) {
-          general(t);
-          if (kEarlyStore && !exact && t == tw && !inexact) {
-            store_rows();
-            stored = true;
-            last_store = t == ntiles && qw < S;
-            ++t;
-            break;
-          }
-        }
-        for (; t <= ntiles; ++t) general(t, stored && t <= tw + 2);
-      } else {
-        for (; t <= ntiles; ++t) {
-          general(t);
-          if (kEarlyStore && !exact && t == tw && !inexact) {
-            store_rows();
-            last_store = t == ntiles && qw < S;
-          }
-        }
-      }
+      const bool last_store = st_step == last && qw < S;
       // No tile load may still be writing this workgroup's LDS when it ends
       // (vmcnt retires in issue order: past the stores of the last step, the
       // loads are in; the next item's prologue waits for the stores).
