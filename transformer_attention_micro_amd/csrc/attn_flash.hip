@@ -208,6 +208,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // The LDS ring: kStages K tiles, then kStages V tiles, each BC x D.
   __shared__ __attribute__((aligned(TB))) bf16_t ring[2 * kStages * BC * D];
   __shared__ int redo_flag;
+  // d <= 64, 8 waves: each wave's 32 query rows staged in LDS (laid out like
+  // the first 32 rows of a K tile), so that Q is read from memory in whole
+  // rows rather than in the 16-byte pieces each lane's fragments take.
+  constexpr bool kQLds = D <= 64 && NW == 8;
+  __shared__ __attribute__((aligned(16))) bf16_t qring[kQLds ? NW * 32 * D : 8];
   auto kst = [&](int j) KB_INLINE { return (lds_bf16 *)(ring + j * BC * D); };
   auto vst = [&](int j) KB_INLINE { return (lds_bf16 *)(ring + (kStages + j) * BC * D); };
 
@@ -242,7 +247,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const size_t base = (size_t)bh * S * D;
 
     bf16x8 qf[KC];
-    {
+    if constexpr (kQLds) {
+      // The wave's rows qw .. qw + 31 are one contiguous block; instruction
+      // c, lane l fills 16-byte slot P = 64 c + l of the wave's LDS block
+      // with chunk (P % CPR) ^ fk(row) of row P / CPR.  Rows past the
+      // sequence end are outside the buffer descriptor and read as zeros.
+      // Waited for (vmcnt) before the prologue's barrier.
+      const uint64_t qa = (uint64_t)(uintptr_t)(Q + base + (size_t)min(qw, S) * D);
+      u32x4 rq;
+      rq.x = __builtin_amdgcn_readfirstlane((uint32_t)qa);
+      rq.y = __builtin_amdgcn_readfirstlane((uint32_t)(qa >> 32) & 0xffffu);
+      rq.z = __builtin_amdgcn_readfirstlane((uint32_t)(max(0, min(32, S - qw)) * 2 * D));
+      rq.w = __builtin_amdgcn_readfirstlane(0x00020000u);
+  #pragma clang diagnostic push
+  #pragma clang diagnostic ignored "-Winline-asm"
+  #pragma unroll
+      for (int c = 0; c < 32 * CPR / 64; ++c) {
+        const int P = 64 * c + lane, row = P / CPR;
+        const uint32_t off = (uint32_t)(row * 2 * D + (((P % CPR) ^ SW::fk(row)) << 4));
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+            (__attribute__((address_space(3))) bf16_t *)(qring + w * 32 * D + c * 512)));
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(m0), "v"(off), "s"(rq) : "memory", "m0");
+      }
+  #pragma clang diagnostic pop
+    } else {
       const bf16_t *qp = Q + base + (size_t)min(q, S - 1) * D + 8 * h;
   #pragma unroll
       for (int kc = 0; kc < KC; ++kc) qf[kc] = *(const bf16x8 *)(qp + 16 * kc);
@@ -931,6 +960,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       load_tile(true, vst(1), 1);
       __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
       wg_barrier();
+      if constexpr (kQLds) {
+        // The B operand fragments of S^T from the wave's staged rows (same
+        // offsets as the K fragments of rows 0 .. 31 of a stage).
+        const lds_char *qb = (const lds_char *)(const lds_bf16 *)(qring + w * 32 * D);
+  #pragma unroll
+        for (int kc = 0; kc < KC; ++kc) qf[kc] = *(const lds_bf16x8 *)(qb + (KL ^ (uint32_t)(kc << 5)));
+      }
       qk(kst(0));
 
       if (exact)
