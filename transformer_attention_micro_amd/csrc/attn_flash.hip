@@ -159,12 +159,12 @@ __device__ __forceinline__ void pin(T &x) {
 // read, the other keeps the matrix core busy.  Problems with fewer 256-query
 // work units than CUs take NW = 4 (128 queries per item, twice the units):
 // the same code, each K/V tile feeding half as many queries, on twice as
-// many CUs (two such workgroups share a CU where their rings fit in LDS).  Per 64-key tile step t a wave has three pieces of
-// work:
+// many CUs (two such workgroups share a CU where their rings fit in LDS).
+// Per 64-key tile step t a wave has three pieces of work:
 //   O^T += V(t-1)^T P(t-1)^T    (MFMA, V from LDS, P from registers)
 //   softmax of tile t           (vector ALU: exponentials, bf16 P; a row
 //                                max only on the first tile and, non-causal,
-//                                the last)
+//                                the last; the first step has no P V yet)
 //   S^T(t+1) = K(t+1) Q^T       (MFMA, K from LDS)
 // and its instruction stream interleaves them, so the vector ALU works in
 // the shadow of the matrix core (a wave keeps issuing independent
@@ -179,7 +179,7 @@ __device__ __forceinline__ void pin(T &x) {
 //
 // LDS: rings of kStages K tiles and kStages V tiles filled by direct
 // global->LDS loads; step t issues K(t+4) and V(t+2), and waits (before its
-// barrier) for the loads of step t-3, which hold K(t+1) and V(t-1).
+// barrier) for the loads of step t-2, which hold K(t+2) and V(t).
 constexpr int kStages = 4;
 
 // s_waitcnt immediate for vmcnt(n), n < 64, other counters left alone.
