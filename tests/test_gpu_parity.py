@@ -295,6 +295,23 @@ def test_flash_scores_outgrowing_the_reference_8_waves(d, causal, jump):
     compare(o, want, p.dtype, f"growing-keys-8w/H{p.H}/d{d}/{'c' if causal else 'nc'}/{'jump' if jump else 'steps'}")
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("scale", [8.0, 256.0])
+def test_flash_last_waves_diagonal_tile_outgrowing_the_reference(d, scale):
+    """Keys from 448 on scaled by 8 (scores tens of log2 units above the
+    reference: the tile is corrected in place) or 256 (the exponentials
+    overflow: the query tile is redone exactly).  Key tile 7 (keys 448..511)
+    is the diagonal tile of waves 6 and 7 of the query tile at 256..511, the
+    waves whose last tile is the item's last: they take that tile's P V in
+    the same step, after its correction.  128 heads at S=1024 causal run
+    8-wave workgroups."""
+    p = inputs.make_problem(1, 128, 1024, d, inputs.BF16, causal=True, seed=13)
+    f = np.where(np.arange(p.S) >= 448, scale, 1.0)
+    p.k[:] = (p.k * f[None, :, None]).astype(np.float32)
+    o = run(p, "flash").cpu().numpy()
+    compare(o, oracle_full(p), p.dtype, f"last-waves-diagonal/d{d}/x{int(scale)}")
+
+
 # A steady tile whose probabilities are each finite but whose sum is not: the
 # scores of every key past the first tile sit about 127.5 log2 units above the
 # reference the first tile sets, so each probability is about 2^127.5 (finite
