@@ -797,9 +797,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // t % 4) and V(t-2) (stage (t + 2) % 4), which are refilled with K(t+4)
     // and V(t+2); K(t+2) and V(t) are now readable, so the end of step t
     // reads the first fragments of step t+1 from them.
-    // `drain` (the steps after a general one, or after the prologue): wait
-    // for every LDS read, since the score products that end such a step read
-    // the K stage that step t refills.
+    // `drain` (general steps and the first step): wait for every LDS read,
+    // since a general step or the prologue before them ends with score
+    // products that read the K stage step t refills.
     // `relax`: the wave issued its 4 MB output stores at the end of step
     // t-1 or t-2, after the loads this wait is for.  vmcnt counts loads and
     // stores together and retires them in issue order, so allowing those
@@ -877,9 +877,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         inexact = true;
       l_run += lsum;
     };
-    // Any step, buffers chosen at run time: the first, the last two of the
-    // wave and the idle steps of causal waves that finished early (each wave
-    // takes part in every step's barrier and loads).
+    // Any step, buffers chosen at run time: every step of the exact pass; in
+    // the fast pass a non-causal item's last two and the steps of causal
+    // waves after their last tile (each wave takes part in every step's
+    // barrier and loads).
     auto general = [&](int t, bool relax = false) KB_INLINE {
       const int st = t & 3;
       begin_step(t, relax, true);
