@@ -41,7 +41,8 @@
 //    registers.  Both on a dispatched grid.
 //  * O and l share a reference m that need not be the running maximum (O / l
 //    does not depend on it in exact arithmetic).  bf16: the first tile
-//    (and, non-causal, the last) takes the exact row maximum; the others
+//    takes the exact row maximum (the reference starts a fixed margin above
+//    it), and, non-causal, so does the last; the others
 //    (a causal wave's diagonal tile among them, masked first) take none
 //    and check the sum of their probabilities instead, correcting the tile
 //    in place (or, if the exponentials overflowed, recomputing the query
@@ -69,6 +70,18 @@ constexpr float kRescaleLog2 = 8.0f;
 // current reference without a row maximum, accepted without redoing the
 // tile exactly; every accepted probability is then at most this.
 constexpr float kSpecLimit = 4096.0f;
+// The fast pass starts each row's reference this many log2 units above the
+// exact maximum of its first tile.  Every probability then carries a common
+// factor 2^-64, which O and l share: O / l is unchanged, and bf16 and fp32
+// keep the same relative precision at that scale.  Probabilities below
+// 2^-62 of the row's largest fall under the fp32 normal range and come out
+// as zero or denormal; at S = 32768 they sum to under 2^-47 of l, so O / l
+// moves by less than 2^-46 of the largest |v|.  The margin leaves headroom for later tiles whose scores
+// outgrow the first tile's: a steady tile fails its sum check only once a
+// row's scores exceed the first tile's maximum by 71 log2 units or more (7
+// without the margin), so rows of large logits (a standard deviation of 8,
+// about 11.5 log2 units) take no in-place corrections.
+constexpr float kRefMargin = 64.0f;
 constexpr int kXcds = 8;
 // s_waitcnt immediate for "vmcnt(0)" with the other counters left alone
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -924,15 +937,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // waited for at the next barrier, which measured faster there.
     constexpr bool kEarlyStore = CAUSAL;
 
-    // Fast pass, step 0: the exact row maximum of tile 0 (the reference for
-    // the steady tiles), then the softmax of tile 0 interleaved with the
-    // score products of tile 1 in the fused instruction stream (no P V yet).
-    // The prologue's score products read stage 0, which this step refills.
+    // Fast pass, step 0: the exact row maximum of tile 0 plus kRefMargin
+    // (the reference for the steady tiles), then the softmax of tile 0
+    // interleaved with the score products of tile 1 in the fused instruction
+    // stream (no P V yet).  The prologue's score products read stage 0, which
+    // this step refills.
     auto step0 = [&]() KB_INLINE {
       begin_step(0, false, true);
       mask(0);
       float alpha;
       row_max(alpha, 0.f);
+      m_run += kRefMargin;
       const uint32_t tk = tile_off(4), tv = tile_off(2);
       auto ld = [&](int k) KB_INLINE {
         if (k < CHW) dma(false, k, kst(0), tk);
