@@ -144,13 +144,17 @@ kb_status kb_triad(float *a, const float *b, const float *c, float s, size_t n, 
  * timed ones, each bracketed by hipEvents recorded on `stream` (so the times
  * cover exactly the kernels of one call, nothing else).  ms_per_iter (host,
  * length iters) receives each call's GPU time; *ms_total the time from the
- * first to the last event.  Synchronises `stream` before returning.
+ * first to the last event.  With ms_per_iter NULL only those two outer
+ * events are recorded and the timed calls follow each other with no event
+ * between them: *ms_total / iters is then the batched mean, which for
+ * kernels of a few microseconds leaves out the cost of the per-call events
+ * (about 3 us per call on MI355X).  Synchronises `stream` before returning.
  * Protocol: kbench page, "The three GPU kernels", last paragraph (events
  * around the kernel only, no host-device copies in the window, configurable
  * warmup, per-launch times for mean / p50 / p99 / min); the warmup also
  * lets the clocks settle ("TileOPs-Metax benchmarks/hardware",
  * "Methodology").  Errors: those of kb_attention (before any launch), and
- * KB_ERR_INVALID for warmup < 0, iters < 1 or NULL result pointers;
+ * KB_ERR_INVALID for warmup < 0, iters < 1 or a NULL ms_total;
  * KB_ERR_HIP if an event call or launch fails (the stream is synchronised
  * first).
  */

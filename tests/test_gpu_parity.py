@@ -395,6 +395,28 @@ def test_repeat_runs_are_bit_identical(variant):
     assert np.array_equal(a, b)
 
 
+def test_bench_batched_mean_without_per_launch_events():
+    """kb_bench_attention with no per-launch array records only the two outer
+    events (the batched mean); the launches still compute the right output,
+    and a NULL total is rejected."""
+    import ctypes
+    torch = torch_cuda()
+    p = inputs.make_problem(1, 4, 300, 64, inputs.BF16, causal=True, seed=5)
+    q, k, v = to_device(p)
+    o = nan_output(p)
+    cfg = kb.make_cfg(p.B, p.H, p.S, p.d, True, kb.KB_BF16)
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
+    per, tot = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, 1, 20)
+    assert len(per) == 20 and all(x > 0 for x in per) and tot >= sum(per) * 0.99
+    o.fill_(float("nan"))
+    per2, tot2 = kb.kb_bench_attention(cfg, *ptrs, "flash", stream, 0, 20, per_launch=False)
+    assert per2 == [] and tot2 > 0
+    compare(o.cpu().numpy(), oracle_full(p), p.dtype, "bench-batched/flash")
+    st = kb.lib().kb_bench_attention(ctypes.byref(cfg), *ptrs, kb.KB_FLASH, stream, 0, 5, None, None)
+    assert st == 1  # KB_ERR_INVALID
+
+
 def test_concurrent_host_threads_match_serial():
     """Four host threads, each on its own stream, run flash on the same
     inputs at once (the ctypes call releases the interpreter lock); every

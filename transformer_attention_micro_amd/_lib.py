@@ -137,12 +137,15 @@ def kb_triad(a: int, b: int, c: int, s: float, n: int, block: int = 256, stream:
 
 
 def kb_bench_attention(cfg: KbAttnCfg, q: int, k: int, v: int, o: int, variant, stream: int,
-                       warmup: int, iters: int):
-    per = (ctypes.c_float * iters)()
+                       warmup: int, iters: int, per_launch: bool = True):
+    """(per-launch ms list, total ms).  per_launch=False records only the two
+    outer events (no event between the launches): the list is then empty and
+    total / iters is the batched mean."""
+    per = (ctypes.c_float * iters)() if per_launch else None
     tot = ctypes.c_float()
     _check(lib().kb_bench_attention(ctypes.byref(cfg), q, k, v, o, _variant(variant), stream or None,
                                     warmup, iters, per, ctypes.byref(tot)), "kb_bench_attention")
-    return list(per), tot.value
+    return (list(per) if per_launch else []), tot.value
 
 
 def kb_bench_triad(a: int, b: int, c: int, s: float, n: int, block: int, stream: int, warmup: int,

@@ -242,10 +242,13 @@ kb_status triad_check(float *a, const float *b, const float *c, size_t n, int32_
 template <typename F>
 kb_status bench_loop(F fn, hipStream_t stream, int32_t warmup, int32_t iters, float *ms_per_iter,
                      float *ms_total) {
-  if (warmup < 0 || iters < 1 || !ms_per_iter || !ms_total) {
-    set_err("warmup >= 0, iters >= 1 and non-NULL result arrays are required");
+  if (warmup < 0 || iters < 1 || !ms_total) {
+    set_err("warmup >= 0, iters >= 1 and a non-NULL ms_total are required");
     return KB_ERR_INVALID;
   }
+  // Without ms_per_iter only the two outer events are recorded: the launches
+  // then follow each other with no event between them (the batched mean).
+  const bool each = ms_per_iter != nullptr;
   for (int i = 0; i < warmup; ++i) {
     kb_status st = fn();
     if (st != KB_OK) return st;
@@ -253,8 +256,9 @@ kb_status bench_loop(F fn, hipStream_t stream, int32_t warmup, int32_t iters, fl
   std::vector<hipEvent_t> ev((size_t)iters + 1, nullptr);
   kb_status st = KB_OK;
   hipError_t e = hipSuccess;
-  for (auto &x : ev) {
-    e = hipEventCreate(&x);
+  for (int i = 0; i <= iters; ++i) {
+    if (!each && i != 0 && i != iters) continue;
+    e = hipEventCreate(&ev[(size_t)i]);
     if (e != hipSuccess) {
       st = hip_fail(e, "hipEventCreate");
       break;
@@ -266,8 +270,10 @@ kb_status bench_loop(F fn, hipStream_t stream, int32_t warmup, int32_t iters, fl
     for (int i = 0; i < iters && st == KB_OK; ++i) {
       st = fn();
       if (st != KB_OK) break;
-      e = hipEventRecord(ev[i + 1], stream);
-      if (e != hipSuccess) st = hip_fail(e, "hipEventRecord");
+      if (each || i + 1 == iters) {
+        e = hipEventRecord(ev[i + 1], stream);
+        if (e != hipSuccess) st = hip_fail(e, "hipEventRecord");
+      }
     }
   }
   if (st == KB_OK) {
@@ -275,7 +281,7 @@ kb_status bench_loop(F fn, hipStream_t stream, int32_t warmup, int32_t iters, fl
     if (e != hipSuccess) st = hip_fail(e, "hipEventSynchronize");
   }
   if (st == KB_OK) {
-    for (int i = 0; i < iters && st == KB_OK; ++i) {
+    for (int i = 0; each && i < iters && st == KB_OK; ++i) {
       e = hipEventElapsedTime(&ms_per_iter[i], ev[i], ev[i + 1]);
       if (e != hipSuccess) st = hip_fail(e, "hipEventElapsedTime");
     }
