@@ -17,6 +17,7 @@ import pytest
 import oracle
 import transformer_attention_micro_amd as kb
 from transformer_attention_micro_amd import inputs
+from tests.flash_cases import diagonal_keys, growing_keys, sum_overflow_problem
 from tests.gpu_util import (TOL, compare, nan_output, oracle_full, oracle_rows, sample_rows, to_device,
                             torch_cuda)
 
@@ -250,28 +251,14 @@ def test_bf16_output(variant):
 
 
 # ------------------------------------------- scores that grow along the key axis
-# The bf16 flash kernel takes most tiles without a row maximum, against the
-# running reference, and checks the tile's probability sums instead.  The
-# reference starts REF_MARGIN log2 units above the first tile's exact
-# maximum.  Keys scaled by powers of two (exact in bf16) make later tiles'
-# scores outgrow the reference: by tens of log2 units (the sum check fails and
-# the tile is corrected in place), or by hundreds (the exponentials overflow
-# and the whole query tile is recomputed exactly).  Which of the two a case
-# reaches was checked on the CPU with a model of the kernel's reference
-# tracking (the growing-keys cases below take 60-270 corrections of their
-# 480-960 steady tiles with this margin).
-REF_MARGIN = 64.0
-
-def _growing_keys(d, causal, jump, S=1024, H=2):
-    p = inputs.make_problem(1, H, S, d, inputs.BF16, causal=causal, seed=11)
-    j = np.arange(p.S)
-    if jump:
-        f = np.where(j >= 320, 256.0, 1.0)
-    else:
-        f = 2.0 ** np.minimum(j // 128, 4)
-    p.k[:] = (p.k * f[None, :, None]).astype(np.float32)
-    return p
-
+# The bf16 flash kernel takes most tiles without a row maximum, against a
+# reference that starts a margin above the first tile's exact maximum, and
+# checks the tile's probability sums instead.  Keys scaled by powers of two
+# (exact in bf16) make later tiles' scores outgrow the reference: by tens of
+# log2 units (the sum check fails and the tile is corrected in place), or by
+# hundreds (the exponentials overflow and the whole query tile is recomputed
+# exactly).  tests/test_reference_model.py checks, on a CPU model of that
+# tracking, which of the two each case below reaches.
 
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
@@ -280,7 +267,7 @@ def _growing_keys(d, causal, jump, S=1024, H=2):
 def test_flash_scores_outgrowing_the_reference(d, causal, jump, S):
     """S = 1000 adds a ragged last tile and a last query tile with rows past
     the sequence end."""
-    p = _growing_keys(d, causal, jump, S)
+    p = growing_keys(d, causal, jump, S)
     o = run(p, "flash").cpu().numpy()
     want = oracle_full(p)
     compare(o, want, p.dtype, f"growing-keys/S{S}/d{d}/{'c' if causal else 'nc'}/{'jump' if jump else 'steps'}")
@@ -294,7 +281,7 @@ def test_flash_scores_outgrowing_the_reference_8_waves(d, causal, jump):
     that the kernel runs 8-wave workgroups on 256-query items: in-place
     corrections and exact redos there, and (causal, d=64) the early output
     stores of waves whose last tile comes before the item's last step."""
-    p = _growing_keys(d, causal, jump, 1024, H=128 if causal else 64)
+    p = growing_keys(d, causal, jump, 1024, H=128 if causal else 64)
     o = run(p, "flash").cpu().numpy()
     want = oracle_full(p)
     compare(o, want, p.dtype, f"growing-keys-8w/H{p.H}/d{d}/{'c' if causal else 'nc'}/{'jump' if jump else 'steps'}")
@@ -311,35 +298,22 @@ def test_flash_last_waves_diagonal_tile_outgrowing_the_reference(d, scale):
     waves whose last tile is the item's last: they take that tile's P V in
     the same step, after its correction.  128 heads at S=1024 causal run
     8-wave workgroups."""
-    p = inputs.make_problem(1, 128, 1024, d, inputs.BF16, causal=True, seed=13)
-    f = np.where(np.arange(p.S) >= 448, scale, 1.0)
-    p.k[:] = (p.k * f[None, :, None]).astype(np.float32)
+    p = diagonal_keys(d, scale)
     o = run(p, "flash").cpu().numpy()
     compare(o, oracle_full(p), p.dtype, f"last-waves-diagonal/d{d}/x{int(scale)}")
 
 
-# A steady tile whose probabilities are each finite but whose sum is not: the
-# scores of every key past the first tile sit 126.4-127.8 log2 units above
-# the reference the first tile sets (its maximum, 0, plus REF_MARGIN), so
-# each probability is at least 2^126.4 and finite in fp32 and in bf16, and a
-# lane's sum of 32 of them overflows fp32.  The correction has to take the
-# sum again from the corrected probabilities; scaling the infinite sum would
-# give l = inf and a zero output.  All queries are 32 e_0; keys 0..63 have a
-# zero first coordinate, the others `a` (bf16-exact values with
-# 32 a * log2(e) / sqrt(d) - REF_MARGIN = 126.4..127.8).
-_SUM_OVERFLOW_A = {32: 23.5, 64: 33.0, 128: 47.0}
-
+# A steady tile whose probabilities are each finite but whose sum is not:
+# the scores of every key past the first tile sit 126.4-127.8 log2 units
+# above the reference, so each probability is finite in fp32 and in bf16 and
+# a lane's sum of 32 of them overflows fp32 (flash_cases.sum_overflow_problem).
+# The correction has to take the sum again from the corrected probabilities;
+# scaling the infinite sum would give l = inf and a zero output.
 
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_flash_steady_tile_sum_overflowing_fp32(d, causal):
-    p = inputs.make_problem(1, 2, 512, d, inputs.BF16, causal=causal, seed=12)
-    x = 32.0 * _SUM_OVERFLOW_A[d] * np.log2(np.e) / np.sqrt(d)
-    assert 123.0 < x - REF_MARGIN < 127.9  # each probability: finite in bf16, 32 of them overflow fp32
-    p.q[:] = 0.0
-    p.q[:, :, 0] = 32.0
-    p.k[:, :64, 0] = 0.0
-    p.k[:, 64:, 0] = _SUM_OVERFLOW_A[d]
+    p = sum_overflow_problem(d, causal)
     o = run(p, "flash").cpu().numpy()
     compare(o, oracle_full(p), p.dtype, f"sum-overflow/d{d}/{'c' if causal else 'nc'}")
 
