@@ -73,7 +73,8 @@ typedef enum {
  *   scale: the logit scale; 0.0f means 1/sqrt(dim).  It is applied in fp32
  *          to the fp32 dot products, never folded into the inputs.
  *   workspace / workspace_bytes: device scratch, used by KB_NAIVE only
- *          (>= kb_attention_workspace_size bytes, 256-byte aligned);
+ *          (>= kb_attention_workspace_size bytes, 256-byte aligned, not
+ *          overlapping Q, K, V or O: KB_ERR_INVALID otherwise);
  *          ignored by the other variants.
  * batch * heads * seq * dim must stay below 2^31 elements per tensor, and
  * batch * heads * seq * seq below 2^40 (naive workspace).

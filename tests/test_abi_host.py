@@ -148,6 +148,16 @@ def test_naive_needs_workspace():
     assert status_of(c, variant="naive") == 3
 
 
+def test_naive_workspace_must_not_overlap_the_tensors():
+    nb = 4 * 2 * 3 * 100 * 100
+    # Q at FAKE (76,800 bytes of bf16), O at 4 FAKE (153,600 bytes of fp32)
+    for ws in (FAKE, FAKE - nb + 256, FAKE * 4 + 1024, FAKE * 3 - 256 * 4):
+        assert status_of(cfg(workspace=ws - ws % 256, workspace_bytes=nb), variant="naive") == 1, ws
+    if not __import__("torch").cuda.is_available():
+        # clear of every tensor: past the argument checks, to the device query
+        assert status_of(cfg(workspace=FAKE * 8, workspace_bytes=nb), variant="naive") == 5
+
+
 def test_valid_call_without_device_reports_no_device():
     import torch
     if torch.cuda.is_available():

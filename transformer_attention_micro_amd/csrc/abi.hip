@@ -192,6 +192,12 @@ kb_status prepare(const kb_attn_cfg *cfg, const void *Q, const void *K, const vo
       set_err("workspace must be 256-byte aligned");
       return KB_ERR_WORKSPACE;
     }
+    const size_t wb = naive_ws_bytes(*p);
+    if (overlap(cfg->workspace, wb, Q, in_bytes) || overlap(cfg->workspace, wb, K, in_bytes) ||
+        overlap(cfg->workspace, wb, V, in_bytes) || overlap(cfg->workspace, wb, O, out_bytes)) {
+      set_err("the workspace overlaps Q, K, V or O");
+      return KB_ERR_INVALID;
+    }
     p->work = (float *)cfg->workspace;
   }
   int lds_limit = 0;
