@@ -62,3 +62,15 @@ def sum_overflow_problem(d, causal):
 def sum_overflow_log2_score(d):
     """The later keys' score in log2 units above the reference."""
     return 32.0 * SUM_OVERFLOW_A[d] * np.log2(np.e) / np.sqrt(d) - REF_MARGIN
+
+
+def first_tile_dominant(d, causal, scale=64.0, S=600, H=3):
+    """Keys 0..63 scaled by `scale` (a power of two): the first tile's row
+    maximum sits well over a hundred log2 units above every later score, so
+    with the margin every later probability falls below the fp32 normal
+    range and underflows; their weight is negligible in the exact result
+    too."""
+    p = inputs.make_problem(1, H, S, d, inputs.BF16, causal=causal, seed=14)
+    f = np.where(np.arange(p.S) < 64, scale, 1.0)
+    p.k[:] = (p.k * f[None, :, None]).astype(np.float32)
+    return p

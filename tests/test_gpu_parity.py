@@ -17,7 +17,7 @@ import pytest
 import oracle
 import transformer_attention_micro_amd as kb
 from transformer_attention_micro_amd import inputs
-from tests.flash_cases import diagonal_keys, growing_keys, sum_overflow_problem
+from tests.flash_cases import diagonal_keys, first_tile_dominant, growing_keys, sum_overflow_problem
 from tests.gpu_util import (TOL, compare, nan_output, oracle_full, oracle_rows, sample_rows, to_device,
                             torch_cuda)
 
@@ -316,6 +316,17 @@ def test_flash_steady_tile_sum_overflowing_fp32(d, causal):
     p = sum_overflow_problem(d, causal)
     o = run(p, "flash").cpu().numpy()
     compare(o, oracle_full(p), p.dtype, f"sum-overflow/d{d}/{'c' if causal else 'nc'}")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_flash_later_probabilities_underflowing_below_the_margin(d, causal):
+    """The first tile's keys scaled by 64: with the reference a margin above
+    its maximum, every later probability underflows (flash_cases), and the
+    output must still match the oracle, finite, on every row."""
+    p = first_tile_dominant(d, causal)
+    o = run(p, "flash").cpu().numpy()
+    compare(o, oracle_full(p), p.dtype, f"first-tile-dominant/d{d}/{'c' if causal else 'nc'}")
 
 
 # ---------------------------------------------------------------- invariants through the GPU

@@ -19,8 +19,8 @@ rounding moves them by far less than the margins these cases leave).
 import numpy as np
 import pytest
 
-from tests.flash_cases import (REF_MARGIN, SPEC_LIMIT, diagonal_keys, growing_keys, sum_overflow_log2_score,
-                               sum_overflow_problem)
+from tests.flash_cases import (REF_MARGIN, SPEC_LIMIT, diagonal_keys, first_tile_dominant, growing_keys,
+                               sum_overflow_log2_score, sum_overflow_problem)
 
 _HALF = (np.arange(64) // 4) % 2  # lane half holding each key of a tile
 
@@ -119,3 +119,17 @@ def test_sum_overflow_case_has_finite_probabilities_and_an_infinite_sum(d, causa
     assert np.all(s[:, :64] == 0.0)  # tile 0 scores 0: the reference is REF_MARGIN
     vis = s[:, 64:128][np.isfinite(s[:, 64:128])]
     assert np.allclose(vis, x + REF_MARGIN)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_first_tile_dominant_case_underflows_every_later_probability(d, causal):
+    p = first_tile_dominant(d, causal)
+    for bh in range(p.BH):
+        rows = np.arange(64, p.S)  # rows with keys past the first tile
+        x = _scores(p, bh, rows)
+        m = np.max(x[:, :64], axis=1) + REF_MARGIN
+        later = x[:, 64:] - m[:, None]
+        assert np.all(later[np.isfinite(later)] < -126.0)  # below the fp32 normal range
+        corr, over = _wave(x[:32], range(1, 4))
+        assert corr == [] and over == []
