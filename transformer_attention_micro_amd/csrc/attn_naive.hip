@@ -22,6 +22,28 @@ using namespace kb;
 namespace {
 
 constexpr int kThreads = 256;
+// Score matrices larger than the 256 MB Infinity Cache leave the caches
+// before the next pass reads them: their stores (pass 1, pass 2) and the
+// softmax pass's loads then carry the non-temporal hint, which keeps them
+// from displacing lines that are still to be used.  Measured (same box,
+// interleaved): B2 H32 S8192 causal -2.3 %, B1 H16 S32768 -2.5 %, B4 H16
+// S2048 causal -11.8 %; at B1 H8 S512 (8 MiB of scores, served from the
+// caches between passes) the hint cost 5.5 %, so small matrices keep plain
+// accesses.  (Pass 3's probability loads take 32-byte pieces of a line per
+// instruction, which the cached path merges: with the hint it was 17 %
+// slower.)
+constexpr size_t kStreamingScoreBytes = (size_t)256 << 20;
+
+template <bool NT, typename T>
+__device__ __forceinline__ void put(T *p, const T &v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ T get(const T *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
 
 // ------------------------------------------------------------- pass 1 -----
 // Workgroup tile: 128 keys j x 128 queries i, computed transposed,
@@ -33,7 +55,7 @@ constexpr int kThreads = 256;
 // tile's space, rows padded to 68 floats) in two halves of 64 keys, so each
 // store instruction writes four whole 256-byte pieces of rows; the pass is
 // bound by these HBM writes.
-template <int D, bool VEC>
+template <int D, bool VEC, bool NT>
 __global__ __launch_bounds__(kThreads) void scores_bf16_kernel(const bf16_t *__restrict__ Q,
                                                                const bf16_t *__restrict__ K,
                                                                float *__restrict__ W, int S,
@@ -94,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void scores_bf16_kernel(const bf16_t *__r
         const int row = 4 * rr + (lane >> 4), col = 4 * (lane & 15);
         const int i = i0 + row, j = j0 + 64 * ph + col;
         const f32x4 val = *(const f32x4 *)&T[row * 68 + col];
-        if (i < S && j + 4 <= S) *(f32x4 *)(W + ((size_t)bh * S + i) * (size_t)S + j) = val;
+        if (i < S && j + 4 <= S) put<NT>((f32x4 *)(W + ((size_t)bh * S + i) * (size_t)S + j), val);
         else if (i < S)
           for (int e = 0; e < 4; ++e)
             if (j + e < S) W[((size_t)bh * S + i) * (size_t)S + j + e] = val[e];
@@ -119,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void scores_bf16_kernel(const bf16_t *__r
 }
 
 // fp32: contraction step (g, e) uses d-column 8g + 4h + e from lane half h.
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(kThreads) void scores_f32_kernel(const float *__restrict__ Q,
                                                               const float *__restrict__ K,
                                                               float *__restrict__ W, int S,
@@ -155,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void scores_f32_kernel(const float *__res
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int i = i0 + acc_row(v, h);
-      if (i < S) wp[(size_t)i * S + j] = acc[jb][v] * scale;
+      if (i < S) put<NT>(&wp[(size_t)i * S + j], acc[jb][v] * scale);
     }
   }
 }
@@ -164,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void scores_f32_kernel(const float *__res
 // One workgroup per row.  Vector path: the row (S % 4 == 0, S <= 1024 * NV)
 // is held in registers as NV float4 per thread, so it is read once and
 // written once.
-template <int NV>
+template <int NV, bool NT>
 __global__ __launch_bounds__(kThreads) void softmax_vec_kernel(float *__restrict__ W, int S,
                                                                int causal) {
   __shared__ float red[kThreads / kWave];
@@ -178,7 +200,8 @@ __global__ __launch_bounds__(kThreads) void softmax_vec_kernel(float *__restrict
   for (int k = 0; k < NV; ++k) {
     const int e = 4 * (threadIdx.x + kThreads * k);
     if (e < S) {
-      x[k] = rp[threadIdx.x + kThreads * k];
+      const f32x4 t = get<NT>((const f32x4 *)&rp[threadIdx.x + kThreads * k]);
+      x[k] = make_float4(t[0], t[1], t[2], t[3]);
       if (e + 0 >= nvis) x[k].x = -INFINITY;
       if (e + 1 >= nvis) x[k].y = -INFINITY;
       if (e + 2 >= nvis) x[k].z = -INFINITY;
@@ -204,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void softmax_vec_kernel(float *__restrict
   for (int k = 0; k < NV; ++k) {
     const int e = 4 * (threadIdx.x + kThreads * k);
     if (e < S)
-      rp[threadIdx.x + kThreads * k] = make_float4(x[k].x * inv, x[k].y * inv, x[k].z * inv, x[k].w * inv);
+      put<NT>((f32x4 *)&rp[threadIdx.x + kThreads * k], f32x4{x[k].x * inv, x[k].y * inv, x[k].z * inv, x[k].w * inv});
   }
 }
 
@@ -401,37 +424,52 @@ __global__ __launch_bounds__(kThreads) void pv_f32_kernel(const float *__restric
   }
 }
 
-template <int D>
-hipError_t launch_scores(const kb_problem &p) {
+bool streaming_scores(const kb_problem &p) {
+  return (size_t)4 * p.bh * (size_t)p.S * (size_t)p.S > kStreamingScoreBytes;
+}
+
+template <int D, bool NT>
+hipError_t launch_scores_nt(const kb_problem &p) {
   const int nt = (p.S + 127) / 128;
   const dim3 grid(nt, nt, p.bh);
   if (p.bf16 && p.S % 4 == 0)
-    hipLaunchKernelGGL((scores_bf16_kernel<D, true>), grid, dim3(kThreads), 0, p.stream,
+    hipLaunchKernelGGL((scores_bf16_kernel<D, true, NT>), grid, dim3(kThreads), 0, p.stream,
                        (const bf16_t *)p.Q, (const bf16_t *)p.K, p.work, p.S, p.scale);
   else if (p.bf16)
-    hipLaunchKernelGGL((scores_bf16_kernel<D, false>), grid, dim3(kThreads), 0, p.stream,
+    hipLaunchKernelGGL((scores_bf16_kernel<D, false, NT>), grid, dim3(kThreads), 0, p.stream,
                        (const bf16_t *)p.Q, (const bf16_t *)p.K, p.work, p.S, p.scale);
   else
-    hipLaunchKernelGGL((scores_f32_kernel<D>), grid, dim3(kThreads), 0, p.stream,
+    hipLaunchKernelGGL((scores_f32_kernel<D, NT>), grid, dim3(kThreads), 0, p.stream,
                        (const float *)p.Q, (const float *)p.K, p.work, p.S, p.scale);
   return hipGetLastError();
 }
 
-hipError_t launch_softmax(const kb_problem &p) {
+template <int D>
+hipError_t launch_scores(const kb_problem &p) {
+  return streaming_scores(p) ? launch_scores_nt<D, true>(p) : launch_scores_nt<D, false>(p);
+}
+
+template <bool NT>
+hipError_t launch_softmax_nt(const kb_problem &p) {
   const size_t rows = (size_t)p.bh * p.S;
   const dim3 grid((unsigned)rows), block(kThreads);
   if (p.S % 4 == 0 && p.S <= 1024 * 32) {
     const int nv = (p.S + 1023) / 1024;
-    if (nv <= 1) hipLaunchKernelGGL(softmax_vec_kernel<1>, grid, block, 0, p.stream, p.work, p.S, p.causal);
-    else if (nv <= 2) hipLaunchKernelGGL(softmax_vec_kernel<2>, grid, block, 0, p.stream, p.work, p.S, p.causal);
-    else if (nv <= 4) hipLaunchKernelGGL(softmax_vec_kernel<4>, grid, block, 0, p.stream, p.work, p.S, p.causal);
-    else if (nv <= 8) hipLaunchKernelGGL(softmax_vec_kernel<8>, grid, block, 0, p.stream, p.work, p.S, p.causal);
-    else if (nv <= 16) hipLaunchKernelGGL(softmax_vec_kernel<16>, grid, block, 0, p.stream, p.work, p.S, p.causal);
-    else hipLaunchKernelGGL(softmax_vec_kernel<32>, grid, block, 0, p.stream, p.work, p.S, p.causal);
+    if (nv <= 1) hipLaunchKernelGGL((softmax_vec_kernel<1, NT>), grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else if (nv <= 2) hipLaunchKernelGGL((softmax_vec_kernel<2, NT>), grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else if (nv <= 4) hipLaunchKernelGGL((softmax_vec_kernel<4, NT>), grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else if (nv <= 8) hipLaunchKernelGGL((softmax_vec_kernel<8, NT>), grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else if (nv <= 16)
+      hipLaunchKernelGGL((softmax_vec_kernel<16, NT>), grid, block, 0, p.stream, p.work, p.S, p.causal);
+    else hipLaunchKernelGGL((softmax_vec_kernel<32, NT>), grid, block, 0, p.stream, p.work, p.S, p.causal);
   } else {
     hipLaunchKernelGGL(softmax_any_kernel, grid, block, 0, p.stream, p.work, p.S, p.causal);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_softmax(const kb_problem &p) {
+  return streaming_scores(p) ? launch_softmax_nt<true>(p) : launch_softmax_nt<false>(p);
 }
 
 template <int D>
