@@ -7,15 +7,21 @@
 // sequence length the kernel supports (4 * S bytes of scores per workgroup).
 //
 // Per row (bh, i), 256 threads:
-//  1. scores  s_j = scale * <q, k_j> for the visible keys: each key row is
-//     read by a group of L lanes with 16-byte loads (L = d * elem / 16), the
-//     partial dot products are summed across the group with lane shuffles,
-//     and the group leader writes s_j to LDS;
+//  1. scores  s_j = scale * <q, k_j> for the visible keys, each written to
+//     LDS by the leader of the lanes that read key row j with 16-byte loads:
+//     bf16, 4 lanes per key, lane k taking the chunks k, k + 4, ... (so each
+//     load instruction reads 64 contiguous bytes of 16 keys' rows), packed
+//     bf16 dot products with fp32 accumulation (v_dot2_f32_bf16: products of
+//     bf16 values are exact in fp32) and a sum over the 4 lanes; fp32, one
+//     lane per 16-byte chunk (L = d / 4 lanes per key), fp32 FMAs and a sum
+//     over the L lanes;
 //  2. m = max_j s_j (wave shuffles, then across the 4 waves through LDS);
 //  3. p_j = 2^((s_j - m) log2 e) in place, l = sum_j p_j;
 //  4. o = sum_j p_j v_j / l: thread (g, c) accumulates 16-byte column chunk c
 //     over keys j = g mod G; the G partial rows are summed through LDS.
 // Everything after the input loads is fp32.
+#include <type_traits>
+
 #include "kb_device.hpp"
 
 using namespace kb;
@@ -69,25 +75,58 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ Q
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int chunk = lane % CPR, sub = lane / CPR;
 
-  float qv[EPC];
-  Elem<T>::unpack(*(const u32x4 *)(Q + base + (size_t)i * D + chunk * EPC), qv);
-
   // 1. scores
   float mloc = -INFINITY;
-  for (int j0 = 0; j0 < nvis; j0 += kWaves * KPW) {
-    const int j = j0 + w * KPW + sub;
-    float dot = 0.f;
-    if (j < nvis) {
-      float kv[EPC];
-      Elem<T>::unpack(*(const u32x4 *)(K + base + (size_t)j * D + chunk * EPC), kv);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    constexpr int LPK = 4, CPL = CPR / LPK, KPS = kWave / LPK;  // lanes / chunks per key, keys per step
+    static_assert(CPR % LPK == 0, "bf16 row chunking");
+    const int k4 = lane % LPK, key = lane / LPK;
+    u32x4 qc[CPL];
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) dot = fmaf(qv[e], kv[e], dot);
+    for (int c = 0; c < CPL; ++c) qc[c] = *(const u32x4 *)(Q + base + (size_t)i * D + (LPK * c + k4) * EPC);
+    for (int j0 = 0; j0 < nvis; j0 += kWaves * KPS) {
+      const int j = j0 + w * KPS + key;
+      float dot = 0.f;
+      if (j < nvis) {
+        const T *kr = K + base + (size_t)j * D;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const u32x4 kv = *(const u32x4 *)(kr + (LPK * c + k4) * EPC);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (through scalars: a bit_cast straight from a vector element
+            // reads element 0)
+            const uint32_t ke = kv[e], qe = qc[c][e];
+            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ke), __builtin_bit_cast(bf16x2, qe), dot,
+                                                  false);
+          }
+        }
+      }
+      dot = group_sum<LPK>(dot);
+      if (j < nvis && k4 == 0) {
+        const float s = dot * scale;
+        sc[j] = s;
+        mloc = fmaxf(mloc, s);
+      }
     }
-    dot = group_sum<CPR>(dot);
-    if (j < nvis && chunk == 0) {
-      const float s = dot * scale;
-      sc[j] = s;
-      mloc = fmaxf(mloc, s);
+  } else {
+    float qv[EPC];
+    Elem<T>::unpack(*(const u32x4 *)(Q + base + (size_t)i * D + chunk * EPC), qv);
+    for (int j0 = 0; j0 < nvis; j0 += kWaves * KPW) {
+      const int j = j0 + w * KPW + sub;
+      float dot = 0.f;
+      if (j < nvis) {
+        float kv[EPC];
+        Elem<T>::unpack(*(const u32x4 *)(K + base + (size_t)j * D + chunk * EPC), kv);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) dot = fmaf(qv[e], kv[e], dot);
+      }
+      dot = group_sum<CPR>(dot);
+      if (j < nvis && chunk == 0) {
+        const float s = dot * scale;
+        sc[j] = s;
+        mloc = fmaxf(mloc, s);
+      }
     }
   }
   __syncthreads();
