@@ -139,6 +139,18 @@ def test_b1h16s32768d128_flash_every_row(part):
         _flash_outputs.pop(name, None)
 
 
+@pytest.mark.parametrize("seed", [1, 2])
+def test_b1h16s32768d128_flash_more_seeds(seed):
+    """The long non-causal workload on two more input draws: tile-edge rows
+    and 64 seeded rows of every head, and a finite output everywhere."""
+    p = inputs.workload("b1h16s32768d128_bf16", seed=seed)
+    rows = sample_rows(p.S, p.BH, seed)
+    want = oracle_rows(p, rows)
+    o = run(p, "flash").cpu().numpy().reshape(p.BH * p.S, p.d)
+    assert np.all(np.isfinite(o)), "non-finite output somewhere"
+    compare(o[rows], want, p.dtype, f"b1h16s32768d128_bf16/seed{seed}/flash")
+
+
 @pytest.mark.parametrize("variant", ("naive", "fused"))
 def test_b1h16s32768d128_bf16(variant):
     p = workload("b1h16s32768d128_bf16")
