@@ -8,13 +8,12 @@
 //
 // Per row (bh, i), 256 threads:
 //  1. scores  s_j = scale * <q, k_j> for the visible keys, each written to
-//     LDS by the leader of the lanes that read key row j with 16-byte loads:
-//     bf16, 4 lanes per key, lane k taking the chunks k, k + 4, ... (so each
-//     load instruction reads 64 contiguous bytes of 16 keys' rows), packed
-//     bf16 dot products with fp32 accumulation (v_dot2_f32_bf16: products of
-//     bf16 values are exact in fp32) and a sum over the 4 lanes; fp32, one
-//     lane per 16-byte chunk (L = d / 4 lanes per key), fp32 FMAs and a sum
-//     over the L lanes;
+//     LDS by the leader of the 4 lanes that read key row j with 16-byte
+//     loads, lane k taking the chunks k, k + 4, ... (so each load
+//     instruction reads 64 contiguous bytes of 16 keys' rows): packed bf16
+//     dot products with fp32 accumulation (v_dot2c_f32_bf16: products of
+//     bf16 values are exact in fp32), or fp32 FMAs, and a sum over the 4
+//     lanes;
 //  2. m = max_j s_j (wave shuffles, then across the 4 waves through LDS);
 //  3. p_j = 2^((s_j - m) log2 e) in place, l = sum_j p_j;
 //  4. o = sum_j p_j v_j / l: thread (g, c) accumulates 16-byte column chunk c
@@ -58,8 +57,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ Q
                                                          const T *__restrict__ V, void *__restrict__ O,
                                                          int out_bf16, int S, int causal, float scale) {
   constexpr int EPC = Elem<T>::kPerChunk;
-  constexpr int CPR = D / EPC;            // 16-byte chunks per row = lanes per key
-  constexpr int KPW = kWave / CPR;        // keys per wave step
+  constexpr int CPR = D / EPC;            // 16-byte chunks per row
   constexpr int G = kThreads / CPR;       // key groups in the P V phase
   static_assert(CPR <= kWave && kWave % CPR == 0, "row chunking");
 
@@ -73,13 +71,16 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ Q
   const int nvis = causal ? i + 1 : S;
   const size_t base = (size_t)bh * S * D;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int chunk = lane % CPR, sub = lane / CPR;
 
-  // 1. scores
+  // 1. scores: 4 lanes per key row, lane k taking the row's 16-byte chunks
+  // k, k + 4, ... (each load instruction reads 64 contiguous bytes of 16
+  // keys' rows); bf16 by packed dot products (v_dot2c_f32_bf16, fp32
+  // accumulation: products of bf16 values are exact in fp32), fp32 by FMAs;
+  // then a shuffle sum over the 4 lanes.
   float mloc = -INFINITY;
-  if constexpr (std::is_same<T, bf16_t>::value) {
+  {
     constexpr int LPK = 4, CPL = CPR / LPK, KPS = kWave / LPK;  // lanes / chunks per key, keys per step
-    static_assert(CPR % LPK == 0, "bf16 row chunking");
+    static_assert(CPR % LPK == 0, "row chunking");
     const int k4 = lane % LPK, key = lane / LPK;
     u32x4 qc[CPL];
 #pragma unroll
@@ -97,32 +98,16 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ Q
             // (through scalars: a bit_cast straight from a vector element
             // reads element 0)
             const uint32_t ke = kv[e], qe = qc[c][e];
-            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ke), __builtin_bit_cast(bf16x2, qe), dot,
-                                                  false);
+            if constexpr (std::is_same<T, bf16_t>::value)
+              dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ke), __builtin_bit_cast(bf16x2, qe),
+                                                    dot, false);
+            else
+              dot = fmaf(__uint_as_float(qe), __uint_as_float(ke), dot);
           }
         }
       }
       dot = group_sum<LPK>(dot);
       if (j < nvis && k4 == 0) {
-        const float s = dot * scale;
-        sc[j] = s;
-        mloc = fmaxf(mloc, s);
-      }
-    }
-  } else {
-    float qv[EPC];
-    Elem<T>::unpack(*(const u32x4 *)(Q + base + (size_t)i * D + chunk * EPC), qv);
-    for (int j0 = 0; j0 < nvis; j0 += kWaves * KPW) {
-      const int j = j0 + w * KPW + sub;
-      float dot = 0.f;
-      if (j < nvis) {
-        float kv[EPC];
-        Elem<T>::unpack(*(const u32x4 *)(K + base + (size_t)j * D + chunk * EPC), kv);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) dot = fmaf(qv[e], kv[e], dot);
-      }
-      dot = group_sum<CPR>(dot);
-      if (j < nvis && chunk == 0) {
         const float s = dot * scale;
         sc[j] = s;
         mloc = fmaxf(mloc, s);
