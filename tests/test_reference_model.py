@@ -16,6 +16,9 @@ infinite probability sends the whole query tile to the exact pass.  Scores
 are taken in float64 from the same bf16-exact inputs (the kernel's fp32
 rounding moves them by far less than the margins these cases leave).
 """
+import re
+from pathlib import Path
+
 import numpy as np
 import pytest
 
@@ -133,3 +136,14 @@ def test_first_tile_dominant_case_underflows_every_later_probability(d, causal):
         assert np.all(later[np.isfinite(later)] < -126.0)  # below the fp32 normal range
         corr, over = _wave(x[:32], range(1, 4))
         assert corr == [] and over == []
+
+
+def test_model_constants_match_the_kernel_source():
+    """The model and the GPU cases restate the kernel's margin and sum limit:
+    if either changes in the kernel, the cases above must be re-derived."""
+    src = (Path(__file__).resolve().parents[1] / "transformer_attention_micro_amd" / "csrc" / "attn_flash.hip").read_text()
+    margin = re.search(r"constexpr float kRefMargin = ([0-9.]+)f;", src)
+    limit = re.search(r"constexpr float kSpecLimit = ([0-9.]+)f;", src)
+    assert margin and limit
+    assert float(margin.group(1)) == REF_MARGIN
+    assert float(limit.group(1)) == SPEC_LIMIT
